@@ -1,0 +1,9 @@
+"""fp64 CPU oracle for fused linear cross-entropy.  TEST INFRASTRUCTURE ONLY:
+imported by tests, the smoke check and the benchmark's CPU-baseline leg, never
+by the HIP library or its Python binding."""
+from .flce_oracle import (ForwardResult, forward, forward_backward, full_pass_with_bias_grad,
+                          logit_grad_block, row_coefficients, sampled_gradients,
+                          transform_logits)
+
+__all__ = ["ForwardResult", "forward", "forward_backward", "full_pass_with_bias_grad",
+           "logit_grad_block", "row_coefficients", "sampled_gradients", "transform_logits"]

@@ -1,0 +1,161 @@
+"""Seeded synthetic inputs for the fused linear cross-entropy workloads.
+
+This module only draws numbers: it holds none of the loss arithmetic, so that
+both the fp64 oracle (``oracle/``) and the HIP path can be fed from it without
+sharing any of the method's code.
+
+Every array is drawn from numpy's PCG64 with a fixed seed.  A workload's seed
+is split with ``SeedSequence.spawn`` into independent streams for hidden,
+weight, bias, targets, the ignore mask and the upstream gradient, so changing
+one recipe never moves another stream.
+
+bf16 inputs are drawn as float32 normals and rounded to bfloat16 with
+round-to-nearest-even; they are carried as their 16-bit patterns
+(``np.uint16``).  ``widen`` turns them (or fp32 arrays) into the exact float64
+values that the oracle consumes.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+IGNORE_INDEX = -100
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    n_tokens: int
+    hidden: int
+    vocab: int
+    dtype: str                      # "f32" | "bf16"
+    weight_std: float
+    bias_std: Optional[float]       # None -> no bias
+    logit_scale: float = 1.0
+    softcap: Optional[float] = None
+    z_loss: float = 0.0
+    ignore_frac: float = 0.0
+    reduction: str = "mean"         # "none" | "sum" | "mean"
+    targets: str = "uniform"        # "uniform" | "zipf"
+    zipf_s: float = 1.1
+    grad_weight_dtype: Optional[str] = None   # None -> same as dtype
+    return_metrics: bool = True
+    seed: int = 0
+
+
+# The five workloads: a tiny fp32 case, a 2k-token bf16 case, a Llama-2-like
+# head, the 128k-vocabulary headline case and a 256k-vocabulary case.
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", 256, 128, 1024, "f32", 0.05, None,
+                          reduction="sum", seed=0),
+    "bf16_n2048_h1024_v32000": Workload(
+        "bf16_n2048_h1024_v32000", 2048, 1024, 32000, "bf16", 0.02, None,
+        ignore_frac=0.10, reduction="mean", seed=1),
+    "bf16_n8192_h4096_v32000_zipf": Workload(
+        "bf16_n8192_h4096_v32000_zipf", 8192, 4096, 32000, "bf16", 0.02, None,
+        z_loss=1e-4, reduction="mean", targets="zipf", seed=2),
+    "bf16_n8192_h4096_v128256": Workload(
+        "bf16_n8192_h4096_v128256", 8192, 4096, 128256, "bf16", 0.02, 0.1,
+        logit_scale=0.5, softcap=30.0, ignore_frac=0.05, reduction="sum", seed=3),
+    "bf16_n16384_h2048_v256000": Workload(
+        "bf16_n16384_h2048_v256000", 16384, 2048, 256000, "bf16", 0.02, None,
+        reduction="none", grad_weight_dtype="f32", seed=4),
+}
+HEADLINE = "bf16_n8192_h4096_v128256"
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_in = x.reshape(-1).view(np.uint32)
+    flat_out = out.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat_in.size, step):
+        u = flat_in[s:s + step]
+        bias = ((u >> 16) & 1) + np.uint32(0x7FFF)
+        flat_out[s:s + step] = ((u + bias) >> 16).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def widen(arr: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
+    """Exact float64 copy of an input array (bf16 bit patterns or float32)."""
+    if arr is None:
+        return None
+    if dtype == "bf16":
+        return bf16_bits_to_f32(arr).astype(np.float64)
+    return arr.astype(np.float64)
+
+
+def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
+    out32 = np.empty(shape, dtype=np.float32)
+    flat = out32.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat.size, step):
+        n = min(step, flat.size - s)
+        flat[s:s + n] = rng.standard_normal(n, dtype=np.float32)
+    if std != 1.0:
+        out32 *= np.float32(std)
+    if dtype == "bf16":
+        return round_to_bf16_bits(out32)
+    return out32
+
+
+def _targets(rng: np.random.Generator, n: int, vocab: int, kind: str, zipf_s: float) -> np.ndarray:
+    if kind == "uniform":
+        return rng.integers(0, vocab, size=n, dtype=np.int64)
+    if kind == "zipf":
+        # finite Zipf on [0, vocab): P(k) proportional to (k+1)^-s, no permutation
+        w = np.arange(1, vocab + 1, dtype=np.float64) ** (-zipf_s)
+        cdf = np.cumsum(w)
+        cdf /= cdf[-1]
+        u = rng.random(n)
+        return np.minimum(np.searchsorted(cdf, u, side="right"), vocab - 1).astype(np.int64)
+    raise ValueError(kind)
+
+
+def make_inputs(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
+                weight_std: float = 0.02, hidden_std: float = 1.0,
+                bias_std: Optional[float] = None, targets: str = "uniform",
+                zipf_s: float = 1.1, ignore_frac: float = 0.0,
+                reduction: str = "mean", seed: int = 0) -> dict:
+    """Draw one problem.  Returns numpy arrays:
+
+    hidden (N,H), weight (V,H), bias (V,) or None -- uint16 bf16 patterns or float32;
+    targets (N,) int64 with exactly floor(ignore_frac*N) entries set to -100;
+    grad_loss: float32 scalar 1.0 for sum/mean, (N,) N(0,1) for "none".
+    """
+    ss = np.random.SeedSequence(seed)
+    s_h, s_w, s_b, s_t, s_i, s_g = ss.spawn(6)
+    out = {
+        "hidden": _normal(np.random.Generator(np.random.PCG64(s_h)), (n_tokens, hidden), hidden_std, dtype),
+        "weight": _normal(np.random.Generator(np.random.PCG64(s_w)), (vocab, hidden), weight_std, dtype),
+        "bias": (None if bias_std is None else
+                 _normal(np.random.Generator(np.random.PCG64(s_b)), (vocab,), bias_std, dtype)),
+    }
+    t = _targets(np.random.Generator(np.random.PCG64(s_t)), n_tokens, vocab, targets, zipf_s)
+    n_ign = int(np.floor(ignore_frac * n_tokens))
+    if n_ign:
+        perm = np.random.Generator(np.random.PCG64(s_i)).permutation(n_tokens)
+        t[perm[:n_ign]] = IGNORE_INDEX
+    out["targets"] = t
+    if reduction == "none":
+        out["grad_loss"] = np.random.Generator(np.random.PCG64(s_g)).standard_normal(
+            n_tokens, dtype=np.float32)
+    else:
+        out["grad_loss"] = np.array(1.0, dtype=np.float32)
+    return out
+
+
+def make_workload_inputs(wl: Workload) -> dict:
+    return make_inputs(wl.n_tokens, wl.hidden, wl.vocab, dtype=wl.dtype,
+                       weight_std=wl.weight_std, bias_std=wl.bias_std,
+                       targets=wl.targets, zipf_s=wl.zipf_s,
+                       ignore_frac=wl.ignore_frac, reduction=wl.reduction,
+                       seed=wl.seed)
