@@ -1,0 +1,188 @@
+"""Benchmark: fused linear cross-entropy forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is flce_forward followed by flce_backward (loss, LSE, metrics, then
+grad_hidden, grad_weight, grad_bias) on the headline workload: N=8192 tokens,
+H=4096, V=128256, bf16, bias, logit_scale 0.5, softcap 30, 5% ignored
+targets, reduction "sum".  Inputs are seeded synthetic data already resident
+in device memory; outputs and workspaces are allocated before timing.
+
+Prints one JSON line.  `value` is tokens/s for the whole step; the step's
+TFLOP/s counts 8*N*H*V (forward logits, recomputed logits and the two
+gradient contractions).  `roofline` reports the forward tile kernel, timed
+with HIP events on the stream it is launched on; `cpu_baseline` times the
+fp64 CPU oracle on a bounded slice of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth_inputs as si  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "fwd+bwd tokens/s and TFLOP/s (8NHV) vs bf16 MFMA peak, N=8192 H=4096 V=128k"
+
+
+def _to_dev(inp, dtype):
+    import torch
+    def dev(a):
+        if a is None:
+            return None
+        if dtype == "bf16" and a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    d = {k: dev(inp[k]) for k in ("hidden", "weight", "bias")}
+    d["targets"] = torch.from_numpy(inp["targets"]).cuda()
+    d["grad_loss"] = torch.from_numpy(np.atleast_1d(inp["grad_loss"]).astype(np.float32)).cuda()
+    return d
+
+
+def cpu_baseline(inp, wl, rows: int):
+    """The fp64 oracle (as is) on the first `rows` tokens of the workload."""
+    import oracle
+    x = si.widen(inp["hidden"][:rows], wl.dtype)
+    w = si.widen(inp["weight"], wl.dtype)
+    b = si.widen(inp["bias"], wl.dtype)
+    t = inp["targets"][:rows]
+    g = inp["grad_loss"][:rows] if wl.reduction == "none" else inp["grad_loss"]
+    t0 = time.perf_counter()
+    oracle.forward_backward(x, w, b, t, np.asarray(g, dtype=np.float64), logit_scale=wl.logit_scale,
+                            softcap=wl.softcap, z_loss=wl.z_loss, reduction=wl.reduction)
+    dt = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward of the first {rows} of {wl.n_tokens} tokens "
+                      f"against the full {wl.vocab}-row weight ({dt:.1f} s)",
+            "seconds": dt, "gflops": 6.0 * rows * wl.hidden * wl.vocab / dt / 1e9}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_cross_entropy_tiled_amd as flce
+
+    flce.load()
+    wl = si.WORKLOADS[args.workload]
+    inp = si.make_workload_inputs(wl)
+    d = _to_dev(inp, wl.dtype)
+    n, h, v = wl.n_tokens, wl.hidden, wl.vocab
+    opts = dict(logit_scale=wl.logit_scale, softcap=wl.softcap, z_loss=wl.z_loss,
+                ignore_index=si.IGNORE_INDEX, reduction=wl.reduction)
+    pf = flce.make_params(n, h, v, dtype=wl.dtype, grad_weight_dtype=wl.grad_weight_dtype, **opts)
+    ws_f = torch.empty(flce.flce_workspace_size(pf, flce.FLCE_PASS_FORWARD), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(flce.flce_workspace_size(pf, flce.FLCE_PASS_BACKWARD), dtype=torch.uint8, device="cuda")
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    loss = torch.empty(n if wl.reduction == "none" else 1, dtype=torch.float32, device="cuda")
+    lse = torch.empty(n, dtype=torch.float32, device="cuda")
+    nc = torch.empty(1, dtype=torch.int64, device="cuda")
+    ent = torch.empty(1, dtype=torch.float32, device="cuda")
+    gh = torch.empty((n, h), dtype=tdt[wl.dtype], device="cuda")
+    gw = torch.empty((v, h), dtype=tdt[wl.grad_weight_dtype or wl.dtype], device="cuda")
+    gb = torch.empty(v, dtype=tdt[wl.dtype], device="cuda") if d["bias"] is not None else None
+    gl = d["grad_loss"] if wl.reduction == "none" else d["grad_loss"][:1]
+    P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def fwd():
+        rc = flce.flce_forward(pf, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]), P(loss),
+                               P(lse), P(nc), P(ent), P(ws_f), ws_f.numel(), sh)
+        if rc:
+            raise flce.FlceError(rc, "flce_forward")
+
+    def bwd():
+        rc = flce.flce_backward(pf, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]), P(lse),
+                                P(gl), P(gh), P(gw), P(gb), P(ws_b), ws_b.numel(), sh)
+        if rc:
+            raise flce.FlceError(rc, "flce_backward")
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        fwd()
+        e1.record(stream)
+        bwd()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    step_ms = wall / args.steps * 1e3
+    flop = 8.0 * n * h * v
+    tflops = flop / (step_ms * 1e-3) / 1e12
+    fwd_tflops = 2.0 * n * h * v / (fwd_ms * 1e-3) / 1e12
+    bwd_tflops = 6.0 * n * h * v / (bwd_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    out = {
+        "metric": METRIC,
+        "value": n / (step_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_tokens": n, "hidden": h, "vocab": v,
+                   "bias": wl.bias_std is not None, "logit_scale": wl.logit_scale, "softcap": wl.softcap,
+                   "z_loss": wl.z_loss, "ignore_frac": wl.ignore_frac, "reduction": wl.reduction,
+                   "grad_weight_dtype": wl.grad_weight_dtype or wl.dtype},
+        "tflops": tflops,
+        "frac_of_peak": tflops / peak,
+        "fwd_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "fwd_tflops": fwd_tflops,
+        "bwd_tflops": bwd_tflops,
+        "peak_mem_gib": torch.cuda.max_memory_allocated() / 2**30,
+        # the forward call is the vocabulary-tiled logit kernel plus two small
+        # finalize kernels; its HIP-event time bounds the tile kernel's time
+        "roofline": {"bound": "mfma", "kernel": "fwd_tiles_kernel (+ finalize)",
+                     "achieved": fwd_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": fwd_tflops / peak, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        del d
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(inp, wl, min(args.cpu_rows, n))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,133 @@
+/*
+ * flce.h -- fused linear cross-entropy for AMD MI355X (gfx950), C ABI.
+ *
+ * The operation (fused-linear-ce README, "Usage" and "Algorithm"; quack-kernels
+ * 0.2.0 quack/linear_cross_entropy.py, linear_cross_entropy_func_ref):
+ *
+ *   u_ij = sum_k hidden_ik * weight_jk + bias_j          (bias optional)
+ *   z_ij = softcap(logit_scale * u_ij)                   softcap(v) = cap*tanh(v/cap), off if cap <= 0
+ *   LSE_i = log sum_j exp(z_ij)
+ *   loss_i = LSE_i - z_{i,t_i} + z_loss * LSE_i^2        for rows with t_i != ignore_index, else 0
+ *   loss = loss_i (none) | sum_i loss_i (sum) | sum_i loss_i / n_valid (mean)
+ *
+ * The (N, V) logits are never written to device memory: the forward pass tiles
+ * the vocabulary and merges each logit tile into a running log-sum-exp, and the
+ * backward pass recomputes the tiles ("Algorithm" section of the README).  The
+ * z-loss term follows the z_loss_multiplier option of the greyhound "Chunked
+ * Linear Cross-Entropy" page ("Usage"); "mean" is one global mean over valid
+ * tokens ("Chunked Linear Loss", "Reduction semantics").
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous, 16-byte
+ *    aligned.  hidden is (N, H), weight (V, H), bias (V) or NULL, targets (N)
+ *    int64.  Floating inputs are all of params->dtype.
+ *  - The caller owns every buffer, including the workspace, which it sizes with
+ *    flce_workspace_size.  The library allocates no device memory and keeps no
+ *    mutable global state; calls on different streams with different
+ *    workspaces may run concurrently.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *    flce_forward and flce_backward never synchronise the host.
+ *  - Every output is overwritten, never accumulated into.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    non-zero status means nothing was launched.
+ *  - Results are deterministic: the same inputs give the same bits, run to run.
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARG = -1,          /* NULL required pointer, negative size, bad enum      */
+  FLCE_ERR_UNSUPPORTED = -2,          /* H % 8 != 0, misaligned pointer, too large a problem */
+  FLCE_ERR_WORKSPACE_TOO_SMALL = -3,
+  FLCE_ERR_HIP = -4,                  /* a HIP runtime call failed                           */
+  FLCE_ERR_TARGET_OUT_OF_RANGE = -5   /* reported by flce_get_status only                    */
+} flce_status;
+
+typedef enum { FLCE_F32 = 0, FLCE_BF16 = 1 } flce_dtype;
+
+typedef enum {
+  FLCE_REDUCTION_NONE = 0,
+  FLCE_REDUCTION_SUM = 1,
+  FLCE_REDUCTION_MEAN = 2
+} flce_reduction;
+
+typedef enum { FLCE_PASS_FORWARD = 0, FLCE_PASS_BACKWARD = 1 } flce_pass;
+
+typedef struct {
+  int64_t n_tokens;           /* N >= 0 (N = 0 is an empty batch)                        */
+  int64_t hidden;             /* H >= 8, H % 8 == 0                                      */
+  int64_t vocab;              /* V >= 1                                                  */
+  int64_t ignore_index;       /* rows whose target equals this are ignored (-100)       */
+  int32_t dtype;              /* flce_dtype of hidden, weight and bias                   */
+  int32_t grad_weight_dtype;  /* flce_dtype of grad_weight; accumulated in fp32 always   */
+  int32_t reduction;          /* flce_reduction                                          */
+  int32_t reserved;           /* must be 0                                               */
+  float logit_scale;          /* multiplies (x.W^T + b); 1.0 = off                       */
+  float softcap;              /* cap of cap*tanh(v/cap); <= 0 = off                      */
+  float z_loss;               /* z-loss multiplier lambda >= 0; 0 = off                  */
+  float reserved_f;           /* must be 0                                               */
+} flce_params;
+
+/* Bytes of device workspace one call of `pass` needs (flce_pass).  Host only. */
+int flce_workspace_size(const flce_params* p, int pass, size_t* bytes);
+
+/*
+ * Forward pass.
+ *  loss:        device fp32, 1 element (sum, mean) or N (none).  Required.
+ *               mean with no valid row gives NaN.
+ *  lse:         device fp32 (N), the per-row log-sum-exp of z, every row
+ *               (ignored rows included).  Required: the backward pass needs it.
+ *  num_correct: device int64 scalar, #valid rows with argmax_j z_ij == t_i
+ *               (ties -> lowest index), or NULL.   (README, "Metrics for free")
+ *  entropy_sum: device fp32 scalar, sum over valid rows of the softmax entropy
+ *               of z in nats, or NULL.
+ * The metrics are always carried through the vocabulary sweep; asking for them
+ * leaves loss and lse bit-identical.
+ * A valid target outside [0, V) is treated as ignored and flags the workspace
+ * status word (see flce_get_status).
+ */
+int flce_forward(const flce_params* p, const void* hidden, const void* weight, const void* bias,
+                 const int64_t* targets, float* loss, float* lse, int64_t* num_correct,
+                 float* entropy_sum, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass: gradients of  sum_i g_i * loss_i  (none) or  g * loss  (sum, mean),
+ * recomputing the logit tiles (README, "Algorithm").
+ *  lse:         device fp32 (N) from flce_forward with the same inputs.
+ *  grad_loss:   device fp32, 1 element (sum, mean) or N (none).
+ *  grad_hidden: device (N, H) in params->dtype.  Required.
+ *  grad_weight: device (V, H) in params->grad_weight_dtype, accumulated in fp32.  Required.
+ *  grad_bias:   device (V) in params->dtype, or NULL; must be NULL when bias is NULL.
+ * Rows whose target is ignored (or out of range) get zero gradient.
+ */
+int flce_backward(const flce_params* p, const void* hidden, const void* weight, const void* bias,
+                  const int64_t* targets, const float* lse, const float* grad_loss,
+                  void* grad_hidden, void* grad_weight, void* grad_bias, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * Synchronises `stream`, then reads the status word that the last forward or
+ * backward call on this workspace left: FLCE_OK, FLCE_ERR_TARGET_OUT_OF_RANGE,
+ * or FLCE_ERR_HIP if the stream reports an error.
+ */
+int flce_get_status(const void* workspace, void* stream);
+
+/* Static text for a status code. */
+const char* flce_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int flce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

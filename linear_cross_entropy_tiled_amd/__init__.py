@@ -1,0 +1,239 @@
+"""Fused linear cross-entropy for AMD MI355X (gfx950): Python binding.
+
+The compute lives in ``libflce.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/flce.h``).  This module only marshals arguments:
+
+* ``flce_workspace_size``, ``flce_forward``, ``flce_backward``,
+  ``flce_get_status``, ``flce_status_string``, ``flce_version`` mirror the C
+  entry points one to one and take raw device pointers (ints);
+* ``forward`` / ``backward`` are torch conveniences that allocate outputs and
+  the workspace with torch and pass the current HIP stream.
+
+There is no fallback: if the library is missing, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libflce.so")
+
+FLCE_OK = 0
+FLCE_ERR_INVALID_ARG = -1
+FLCE_ERR_UNSUPPORTED = -2
+FLCE_ERR_WORKSPACE_TOO_SMALL = -3
+FLCE_ERR_HIP = -4
+FLCE_ERR_TARGET_OUT_OF_RANGE = -5
+
+FLCE_F32 = 0
+FLCE_BF16 = 1
+REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
+FLCE_PASS_FORWARD = 0
+FLCE_PASS_BACKWARD = 1
+
+EXPORTED = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_get_status",
+            "flce_status_string", "flce_version")
+
+
+class flce_params(ctypes.Structure):
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64),
+        ("hidden", ctypes.c_int64),
+        ("vocab", ctypes.c_int64),
+        ("ignore_index", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("grad_weight_dtype", ctypes.c_int32),
+        ("reduction", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("logit_scale", ctypes.c_float),
+        ("softcap", ctypes.c_float),
+        ("z_loss", ctypes.c_float),
+        ("reserved_f", ctypes.c_float),
+    ]
+
+
+class FlceError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {status_string(code)} ({code})")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load libflce.so (once).  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m linear_cross_entropy_tiled_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(flce_params)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.flce_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.flce_workspace_size.restype = ctypes.c_int
+    lib.flce_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.flce_forward.restype = ctypes.c_int
+    lib.flce_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.flce_backward.restype = ctypes.c_int
+    lib.flce_get_status.argtypes = [vp, vp]
+    lib.flce_get_status.restype = ctypes.c_int
+    lib.flce_status_string.argtypes = [ctypes.c_int]
+    lib.flce_status_string.restype = ctypes.c_char_p
+    lib.flce_version.argtypes = []
+    lib.flce_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------------------- raw C entry points
+
+def flce_workspace_size(params: flce_params, pass_: int) -> int:
+    out = ctypes.c_size_t(0)
+    rc = load().flce_workspace_size(ctypes.byref(params), pass_, ctypes.byref(out))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_workspace_size")
+    return out.value
+
+
+def flce_forward(params, hidden, weight, bias, targets, loss, lse, num_correct, entropy_sum,
+                 workspace, workspace_bytes, stream) -> int:
+    return load().flce_forward(ctypes.byref(params), hidden, weight, bias, targets, loss, lse,
+                               num_correct, entropy_sum, workspace, workspace_bytes, stream)
+
+
+def flce_backward(params, hidden, weight, bias, targets, lse, grad_loss, grad_hidden, grad_weight,
+                  grad_bias, workspace, workspace_bytes, stream) -> int:
+    return load().flce_backward(ctypes.byref(params), hidden, weight, bias, targets, lse, grad_loss,
+                                grad_hidden, grad_weight, grad_bias, workspace, workspace_bytes,
+                                stream)
+
+
+def flce_get_status(workspace, stream) -> int:
+    return load().flce_get_status(workspace, stream)
+
+
+def flce_status_string(code: int) -> str:
+    return load().flce_status_string(code).decode()
+
+
+def flce_version() -> int:
+    return load().flce_version()
+
+
+def status_string(code: int) -> str:
+    try:
+        return flce_status_string(code)
+    except Exception:
+        return "status"
+
+
+# ----------------------------------------------------------------------------- torch conveniences
+
+def make_params(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
+                grad_weight_dtype: Optional[str] = None, logit_scale: float = 1.0,
+                softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
+                reduction: str = "mean") -> flce_params:
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"invalid reduction {reduction!r}")
+    dt = {"bf16": FLCE_BF16, "f32": FLCE_F32}
+    p = flce_params()
+    p.n_tokens, p.hidden, p.vocab, p.ignore_index = n_tokens, hidden, vocab, ignore_index
+    p.dtype = dt[dtype]
+    p.grad_weight_dtype = dt[grad_weight_dtype or dtype]
+    p.reduction = REDUCTIONS[reduction]
+    p.logit_scale = logit_scale
+    p.softcap = softcap if softcap else 0.0
+    p.z_loss = z_loss
+    return p
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_name(t) -> str:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float32:
+        return "f32"
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(t, name):
+    if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def forward(hidden, weight, targets, bias=None, *, logit_scale: float = 1.0,
+            softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
+            reduction: str = "mean", return_metrics: bool = False, workspace=None):
+    """Runs flce_forward on the current stream.  Returns (loss, lse, metrics | None)."""
+    import torch
+    for t, n in ((hidden, "hidden"), (weight, "weight"), (targets, "targets"), (bias, "bias")):
+        _check(t, n)
+    n, h = hidden.shape
+    v = weight.shape[0]
+    p = make_params(n, h, v, dtype=_dtype_name(hidden), logit_scale=logit_scale, softcap=softcap,
+                    z_loss=z_loss, ignore_index=ignore_index, reduction=reduction)
+    dev = hidden.device
+    ws_bytes = flce_workspace_size(p, FLCE_PASS_FORWARD)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    loss = torch.empty(n if reduction == "none" else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    nc = torch.empty(1, dtype=torch.int64, device=dev) if return_metrics else None
+    ent = torch.empty(1, dtype=torch.float32, device=dev) if return_metrics else None
+    rc = flce_forward(p, _ptr(hidden), _ptr(weight), _ptr(bias), _ptr(targets), _ptr(loss), _ptr(lse),
+                      _ptr(nc), _ptr(ent), _ptr(workspace), workspace.numel(), _stream_handle(dev))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_forward")
+    if reduction != "none":
+        loss = loss.reshape(())
+    metrics = {"num_correct_tokens": nc.reshape(()), "entropy_sum": ent.reshape(())} if return_metrics else None
+    return loss, lse, metrics
+
+
+def backward(hidden, weight, targets, lse, grad_loss, bias=None, *, logit_scale: float = 1.0,
+             softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
+             reduction: str = "mean", grad_weight_dtype: Optional[str] = None, workspace=None):
+    """Runs flce_backward on the current stream.  Returns (grad_hidden, grad_weight, grad_bias)."""
+    import torch
+    for t, n in ((hidden, "hidden"), (weight, "weight"), (targets, "targets"), (bias, "bias"),
+                 (lse, "lse"), (grad_loss, "grad_loss")):
+        _check(t, n)
+    n, h = hidden.shape
+    v = weight.shape[0]
+    dt = _dtype_name(hidden)
+    p = make_params(n, h, v, dtype=dt, grad_weight_dtype=grad_weight_dtype, logit_scale=logit_scale,
+                    softcap=softcap, z_loss=z_loss, ignore_index=ignore_index, reduction=reduction)
+    dev = hidden.device
+    ws_bytes = flce_workspace_size(p, FLCE_PASS_BACKWARD)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    gh = torch.empty((n, h), dtype=hidden.dtype, device=dev)
+    gw = torch.empty((v, h), dtype=tdt[grad_weight_dtype or dt], device=dev)
+    gb = torch.empty(v, dtype=bias.dtype, device=dev) if bias is not None else None
+    rc = flce_backward(p, _ptr(hidden), _ptr(weight), _ptr(bias), _ptr(targets), _ptr(lse),
+                       _ptr(grad_loss), _ptr(gh), _ptr(gw), _ptr(gb), _ptr(workspace),
+                       workspace.numel(), _stream_handle(dev))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_backward")
+    return gh, gw, gb
+
+
+def get_status(workspace) -> int:
+    return flce_get_status(_ptr(workspace), _stream_handle(workspace.device))

@@ -1,0 +1,181 @@
+// C ABI of the fused linear cross-entropy library: argument validation,
+// planning (tile counts, vocabulary splits and chunks, workspace layout) and
+// the entry points.  Validation runs on the host before any HIP call.
+#include <math.h>
+#include <string.h>
+
+#include "flce_internal.h"
+
+namespace flce {
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Scratch budget for the dlogits chunk (N_pad x Vc elements).
+static constexpr size_t kDlogitsBudget = size_t(512) << 20;
+static constexpr int64_t kMaxChunkTiles = 128;
+// Number of compute units the forward split count is sized for (MI355X).
+static constexpr int64_t kTargetWorkgroups = 256;
+
+int make_plan(const flce_params* p, Plan* pl) {
+  if (!p || !pl) return FLCE_ERR_INVALID_ARG;
+  if (p->n_tokens < 0 || p->hidden <= 0 || p->vocab <= 0) return FLCE_ERR_INVALID_ARG;
+  if (p->dtype != FLCE_F32 && p->dtype != FLCE_BF16) return FLCE_ERR_INVALID_ARG;
+  if (p->grad_weight_dtype != FLCE_F32 && p->grad_weight_dtype != FLCE_BF16) return FLCE_ERR_INVALID_ARG;
+  if (p->reduction != FLCE_REDUCTION_NONE && p->reduction != FLCE_REDUCTION_SUM &&
+      p->reduction != FLCE_REDUCTION_MEAN)
+    return FLCE_ERR_INVALID_ARG;
+  if (p->reserved != 0 || p->reserved_f != 0.0f) return FLCE_ERR_INVALID_ARG;
+  if (!isfinite(p->logit_scale) || !isfinite(p->softcap) || !isfinite(p->z_loss) || p->z_loss < 0.0f)
+    return FLCE_ERR_INVALID_ARG;
+  if (p->hidden % 8 != 0) return FLCE_ERR_UNSUPPORTED;
+  const int esize = p->dtype == FLCE_BF16 ? 2 : 4;
+  // 32-bit buffer offsets and int indices inside the kernels
+  if (p->n_tokens > (int64_t(1) << 30) || p->vocab > (int64_t(1) << 30) || p->hidden > (int64_t(1) << 20))
+    return FLCE_ERR_UNSUPPORTED;
+  if (p->n_tokens * p->hidden * esize >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+
+  Plan& P = *pl;
+  memset(&P, 0, sizeof(P));
+  P.N = p->n_tokens;
+  P.H = p->hidden;
+  P.V = p->vocab;
+  P.ignore_index = p->ignore_index;
+  P.dtype = p->dtype;
+  P.gw_dtype = p->grad_weight_dtype;
+  P.reduction = p->reduction;
+  P.scale = p->logit_scale;
+  P.cap = p->softcap > 0.0f ? p->softcap : 0.0f;
+  P.z_loss = p->z_loss;
+  P.esize = esize;
+  P.n_tt = (P.N + 255) / 256;
+  P.n_vt = (P.V + 255) / 256;
+  P.n_ht = (P.H + 255) / 256;
+  P.N_pad = P.n_tt * 256;
+  P.V_pad = P.n_vt * 256;
+
+  // forward: split the vocabulary so that about one workgroup runs per CU
+  int64_t S = P.n_tt > 0 ? (kTargetWorkgroups + P.n_tt / 2) / P.n_tt : 1;
+  if (S < 1) S = 1;
+  if (S > P.n_vt) S = P.n_vt;
+  P.S = (int)S;
+  P.f_part = kStatusBytes;
+  const size_t part_bytes = size_t(5) * S * P.N_pad * 4;
+  P.f_blk = align_up(P.f_part + part_bytes, 256);
+  const int64_t nblk = P.N > 0 ? (P.N + 255) / 256 : 1;
+  P.f_bytes = align_up(P.f_blk + size_t(nblk) * sizeof(BlockPart), 256);
+
+  // backward: vocabulary chunks whose dlogits scratch fits the budget
+  int64_t max_tiles = kMaxChunkTiles;
+  if (P.N_pad > 0) {
+    const int64_t fit = (int64_t)(kDlogitsBudget / (size_t(P.N_pad) * esize * 256));
+    if (fit < max_tiles) max_tiles = fit;
+  }
+  if (max_tiles < 1) max_tiles = 1;
+  P.n_chunks = (int)((P.n_vt + max_tiles - 1) / max_tiles);
+  const int64_t tiles_per_chunk = (P.n_vt + P.n_chunks - 1) / P.n_chunks;
+  P.Vc = tiles_per_chunk * 256;
+  if (P.Vc * P.H * esize >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+  if (P.N_pad * P.Vc * esize >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+  size_t o = kStatusBytes;
+  P.b_coefA = o;
+  o = align_up(o + size_t(P.N_pad) * 4, 256);
+  P.b_coefB = o;
+  o = align_up(o + size_t(P.N_pad) * 4, 256);
+  P.b_lseL = o;
+  o = align_up(o + size_t(P.N_pad) * 4, 256);
+  P.b_tgt = o;
+  o = align_up(o + size_t(P.N_pad) * 4, 256);
+  P.b_D = o;
+  o = align_up(o + size_t(P.N_pad) * P.Vc * esize, 256);
+  P.b_ghacc = o;
+  if (P.dtype == FLCE_BF16 && P.n_chunks > 1) o = align_up(o + size_t(P.N) * P.H * 4, 256);
+  P.b_gbpart = o;
+  o = align_up(o + size_t(P.n_tt) * P.V_pad * 4, 256);
+  P.b_bytes = o;
+  return FLCE_OK;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace flce
+
+using namespace flce;
+
+extern "C" {
+
+int flce_version(void) { return 100; }
+
+const char* flce_status_string(int s) {
+  switch (s) {
+    case FLCE_OK: return "ok";
+    case FLCE_ERR_INVALID_ARG: return "invalid argument";
+    case FLCE_ERR_UNSUPPORTED: return "unsupported shape, alignment or size";
+    case FLCE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FLCE_ERR_HIP: return "HIP runtime error";
+    case FLCE_ERR_TARGET_OUT_OF_RANGE: return "a target is outside [0, vocab) and not ignore_index";
+    default: return "unknown status";
+  }
+}
+
+int flce_workspace_size(const flce_params* p, int pass, size_t* bytes) {
+  if (!bytes) return FLCE_ERR_INVALID_ARG;
+  Plan pl;
+  const int rc = make_plan(p, &pl);
+  if (rc != FLCE_OK) return rc;
+  if (pass == FLCE_PASS_FORWARD) *bytes = pl.f_bytes;
+  else if (pass == FLCE_PASS_BACKWARD) *bytes = pl.b_bytes;
+  else return FLCE_ERR_INVALID_ARG;
+  return FLCE_OK;
+}
+
+int flce_forward(const flce_params* p, const void* hidden, const void* weight, const void* bias,
+                 const int64_t* targets, float* loss, float* lse, int64_t* num_correct,
+                 float* entropy_sum, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  int rc = make_plan(p, &pl);
+  if (rc != FLCE_OK) return rc;
+  pl.has_bias = bias != nullptr;
+  if (!workspace) return FLCE_ERR_INVALID_ARG;
+  if (!loss && (pl.reduction != FLCE_REDUCTION_NONE || pl.N > 0)) return FLCE_ERR_INVALID_ARG;
+  if (pl.N > 0 && (!hidden || !targets || !lse)) return FLCE_ERR_INVALID_ARG;
+  if (!weight) return FLCE_ERR_INVALID_ARG;
+  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(bias) || !aligned16(workspace) ||
+      !aligned16(targets))
+    return FLCE_ERR_UNSUPPORTED;
+  if (workspace_bytes < pl.f_bytes) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  hipError_t e = launch_forward(pl, hidden, weight, bias, targets, loss, lse, num_correct, entropy_sum,
+                                static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+int flce_backward(const flce_params* p, const void* hidden, const void* weight, const void* bias,
+                  const int64_t* targets, const float* lse, const float* grad_loss, void* grad_hidden,
+                  void* grad_weight, void* grad_bias, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  Plan pl;
+  int rc = make_plan(p, &pl);
+  if (rc != FLCE_OK) return rc;
+  pl.has_bias = bias != nullptr;
+  if (!weight || !grad_weight || !workspace) return FLCE_ERR_INVALID_ARG;
+  if (!grad_loss && (pl.reduction != FLCE_REDUCTION_NONE || pl.N > 0)) return FLCE_ERR_INVALID_ARG;
+  if (pl.N > 0 && (!hidden || !targets || !lse || !grad_hidden)) return FLCE_ERR_INVALID_ARG;
+  if (grad_bias && !bias) return FLCE_ERR_INVALID_ARG;
+  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(bias) || !aligned16(workspace) ||
+      !aligned16(targets) || !aligned16(grad_hidden) || !aligned16(grad_weight) || !aligned16(grad_bias))
+    return FLCE_ERR_UNSUPPORTED;
+  if (workspace_bytes < pl.b_bytes) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  hipError_t e = launch_backward(pl, hidden, weight, bias, targets, lse, grad_loss, grad_hidden,
+                                 grad_weight, grad_bias, static_cast<char*>(workspace),
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+int flce_get_status(const void* workspace, void* stream) {
+  if (!workspace) return FLCE_ERR_INVALID_ARG;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return FLCE_ERR_HIP;
+  int v = 0;
+  if (hipMemcpy(&v, workspace, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return FLCE_ERR_HIP;
+  return v;
+}
+
+}  // extern "C"

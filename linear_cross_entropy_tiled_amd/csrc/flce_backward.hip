@@ -1,0 +1,527 @@
+// Backward pass: recompute each logit tile, form the logit gradient, and feed
+// the two gradient contractions, one vocabulary chunk at a time.
+//
+// Method: fused-linear-ce README, "Algorithm" (recompute each tile, form
+// p - onehot, accumulate grad_hidden = (p - onehot) @ weight and
+// grad_weight = (p - onehot)^T @ hidden).  The weight gradient is accumulated
+// in fp32 and cast once ("Chunked Linear Loss", "Weight-gradient accumulation
+// dtype").  Per vocabulary chunk of width Vc:
+//   dlogits  D[t][v] = scale * softcap'(z) * c_t * ((1 + 2 lam LSE_t) p_tv - [v = t_t])
+//            into a scratch of N x Vc (bf16 for bf16 inputs), plus per
+//            token-tile column sums of D for grad_bias;
+//   gw       grad_weight[v][:] = sum_t D[t][v] hidden[t][:]    (written once per row);
+//   gh       grad_hidden[t][:] += sum_v D[t][v] weight[v][:]   (fp32, fixed chunk order).
+// No float atomics: every output element has exactly one writer per launch,
+// so results are bitwise reproducible.
+#include "flce_device.h"
+#include "flce_internal.h"
+
+namespace flce {
+
+// ---------------------------------------------------------------------------
+// Per-row coefficients: n_valid, c_i, and the constants the dlogits epilogue
+// needs.  One block; N is at most a few hundred thousand rows.
+// ---------------------------------------------------------------------------
+struct PrepArgs {
+  const int64_t* targets;
+  const float* lse;
+  const float* grad_loss;
+  int N, V, N_pad, reduction;
+  int64_t ignore_index;
+  float z_loss;
+  float* coefA;   // c_i (1 + 2 lam LSE_i), 0 if ignored
+  float* coefB;   // c_i, 0 if ignored
+  float* lseL;    // LSE_i * log2(e)
+  int* tgt;       // target or -1
+  int* status;
+};
+
+__global__ __launch_bounds__(1024) void bwd_prep_kernel(PrepArgs a) {
+  __shared__ int sv[1024], sb[1024];
+  const int tid = threadIdx.x;
+  int nv = 0, bad = 0;
+  for (int i = tid; i < a.N; i += 1024) {
+    const int64_t t = a.targets[i];
+    const bool in_range = t >= 0 && t < a.V;
+    nv += (t != a.ignore_index && in_range) ? 1 : 0;
+    bad |= (t != a.ignore_index && !in_range) ? 1 : 0;
+  }
+  sv[tid] = nv;
+  sb[tid] = bad;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (tid < w) {
+      sv[tid] += sv[tid + w];
+      sb[tid] |= sb[tid + w];
+    }
+    __syncthreads();
+  }
+  const int n_valid = sv[0];
+  const float g0 = a.reduction == FLCE_REDUCTION_NONE ? 0.0f : a.grad_loss[0];
+  const float c_all = a.reduction == FLCE_REDUCTION_SUM ? g0 : (n_valid > 0 ? g0 / (float)n_valid : 0.0f);
+  for (int i = tid; i < a.N_pad; i += 1024) {
+    float ca = 0.0f, cb = 0.0f, ll = 0.0f;
+    int tg = -1;
+    if (i < a.N) {
+      const int64_t t = a.targets[i];
+      const bool valid = t != a.ignore_index && t >= 0 && t < a.V;
+      const float lse = a.lse[i];
+      ll = lse * kLog2e;
+      if (valid) {
+        const float c = a.reduction == FLCE_REDUCTION_NONE ? a.grad_loss[i] : c_all;
+        ca = c * (1.0f + 2.0f * a.z_loss * lse);
+        cb = c;
+        tg = (int)t;
+      }
+    }
+    a.coefA[i] = ca;
+    a.coefB[i] = cb;
+    a.lseL[i] = ll;
+    a.tgt[i] = tg;
+  }
+  if (tid == 0) a.status[0] = sb[0] ? FLCE_ERR_TARGET_OUT_OF_RANGE : FLCE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Stores of 4 consecutive values (one lane, 4 consecutive rows of a tile).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (bf16)a;
+  v[1] = (bf16)b;
+  v[2] = (bf16)c;
+  v[3] = (bf16)d;
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  f32x4 v;
+  v[0] = a;
+  v[1] = b;
+  v[2] = c;
+  v[3] = d;
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+template <typename T>
+__device__ __forceinline__ void load_bias4_bwd(const T* b, int r0, int V, float* out) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) out[j] = (r0 + j < V) ? load_elem<T>(b, r0 + j) : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// dlogits: one 256 (vocab) x 256 (token) tile per workgroup.
+// ---------------------------------------------------------------------------
+struct DlogitsArgs {
+  const char* hidden;
+  const char* weight;
+  const void* bias;
+  int N, H, V;
+  float scale, cap, two_log2e_over_cap, two_cap, neg_scale_over_cap2;
+  int cv0;          // first vocabulary row of the chunk
+  int n_vt_c;       // vocabulary tiles in the chunk
+  int n_tt;
+  const float* coefA;
+  const float* coefB;
+  const float* lseL;
+  const int* tgt;
+  void* D;          // D[t][v - cv0], row stride ldD elements
+  int ldD;
+  float* gb_part;   // [n_tt][ld_gb]
+  int ld_gb;
+};
+
+template <typename T, bool HAS_BIAS, bool SOFTCAP>
+__global__ __launch_bounds__(256, 1) void bwd_dlogits_kernel(DlogitsArgs a) {
+  constexpr int E = sizeof(T);
+  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  int vt, tt;
+  grouped_tile(L, a.n_vt_c, a.n_tt, 4, vt, tt);
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int v0 = a.cv0 + vt * 256, t0 = tt * 256;
+
+  const uint32_t ld = (uint32_t)a.H * E;
+  OperandDesc da, db;
+  da.base = a.weight + (size_t)v0 * ld;
+  da.ld_bytes = ld;
+  da.nrec = (uint32_t)max(min(a.V - v0, 256), 0) * ld;
+  da.cols_valid = 0;
+  da.k_bytes = a.H * E;
+  db.base = a.hidden + (size_t)t0 * ld;
+  db.ld_bytes = ld;
+  db.nrec = (uint32_t)max(min(a.N - t0, 256), 0) * ld;
+  db.cols_valid = 0;
+  db.k_bytes = a.H * E;
+  const int KT = (a.H * E + kBKB - 1) / kBKB;
+
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  tile_mainloop<T, true, true>(da, db, KT, acc);
+
+  // ---- epilogue, one 32-row MFMA tile at a time:
+  //   D = scale * softcap'(z) * (coefA * p - [row = target] * coefB),
+  // stored as 4 consecutive vocabulary rows per lane, plus the column sums
+  // over this tile's 256 tokens for grad_bias
+  const int vw = v0 + wm * 128;
+  const bool ragged = vw + 128 > a.V;
+  float cA[4], cB[4], lL[4];
+  int rel[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ni++) {
+    const int t = t0 + wn * 128 + ni * 32 + (lane & 31);
+    cA[ni] = a.coefA[t];
+    cB[ni] = a.coefB[t];
+    lL[ni] = a.lseL[t];
+    rel[ni] = a.tgt[t] - vw;
+  }
+  T* D = reinterpret_cast<T*>(a.D);
+  float* xs = reinterpret_cast<float*>(g_stage0);   // [wm][mi][64 lanes]: column sums of the wn = 1 waves
+  float gsum[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; mi++) {
+    float sb[16];
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      float b4[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (HAS_BIAS)
+        load_bias4_bwd<T>(reinterpret_cast<const T*>(a.bias), vw + mi * 32 + 8 * g + 4 * (lane >> 5), a.V, b4);
+#pragma unroll
+      for (int j = 0; j < 4; j++) sb[4 * g + j] = a.scale * b4[j];
+    }
+    float cs[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) cs[r] = 0.0f;
+#pragma unroll
+    for (int ni = 0; ni < 4; ni++) {
+      float d[16];
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        float z = HAS_BIAS ? fmaf(acc[mi][ni][r], a.scale, sb[r]) : acc[mi][ni][r] * a.scale;
+        if constexpr (SOFTCAP) z = softcap_apply(z, a.two_log2e_over_cap, a.cap, a.two_cap);
+        const int row = acc_row(mi, r, lane);
+        const float p = fast_exp2(fmaf(z, kLog2e, -lL[ni]));
+        float v = fmaf(cA[ni], p, row == rel[ni] ? -cB[ni] : 0.0f);
+        if constexpr (SOFTCAP) v *= fmaf(z * z, a.neg_scale_over_cap2, a.scale);
+        else v *= a.scale;
+        if (ragged && vw + row >= a.V) v = 0.0f;
+        d[r] = v;
+        cs[r] += v;
+      }
+      const int t = t0 + wn * 128 + ni * 32 + (lane & 31);
+      T* drow = D + (size_t)t * a.ldD + (vw - a.cv0) + mi * 32 + 4 * (lane >> 5);
+#pragma unroll
+      for (int g = 0; g < 4; g++) store4(drow + 8 * g, d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]);
+    }
+    if constexpr (HAS_BIAS) {
+      // reduce-scatter the 16 column sums over the 32 lanes of each half;
+      // afterwards lanes 2j and 2j+1 both hold the sum of position r = j
+#pragma unroll
+      for (int n = 8, m = 16; m >= 2; n >>= 1, m >>= 1) {
+        const bool up = (lane & m) != 0;
+#pragma unroll
+        for (int p = 0; p < n; p++) {
+          const float keep = up ? cs[p + n] : cs[p];
+          const float send = up ? cs[p] : cs[p + n];
+          cs[p] = keep + __shfl_xor(send, m);
+        }
+      }
+      gsum[mi] = cs[0] + __shfl_xor(cs[0], 1);
+    }
+  }
+  if constexpr (HAS_BIAS) {
+    if (wn == 1) {
+#pragma unroll
+      for (int mi = 0; mi < 4; mi++) xs[(wm * 4 + mi) * 64 + lane] = gsum[mi];
+    }
+    __syncthreads();
+    if (wn == 0 && (lane & 1) == 0) {
+#pragma unroll
+      for (int mi = 0; mi < 4; mi++) {
+        const int row = acc_row(mi, (lane & 31) >> 1, lane);
+        a.gb_part[(size_t)tt * a.ld_gb + vw + row] = gsum[mi] + xs[(wm * 4 + mi) * 64 + lane];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// grad_weight for one chunk: C[h][v] = sum_t hidden[t][h] D[t][v]
+// A = hidden (MNMAJOR: rows t, cols h), B = D (MNMAJOR: rows t, cols v).
+// ---------------------------------------------------------------------------
+struct GwArgs {
+  const char* hidden;
+  const char* D;
+  int ldD;
+  int N, H, V, N_pad;
+  int cv0;
+  int n_ht, n_vt_c;
+  void* gw;
+  int gw_f32;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void bwd_gw_kernel(GwArgs a) {
+  constexpr int E = sizeof(T);
+  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  int ht, vt;
+  grouped_tile(L, a.n_ht, a.n_vt_c, 4, ht, vt);
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h0 = ht * 256, vl0 = vt * 256;
+
+  OperandDesc da, db;
+  const uint32_t ldh = (uint32_t)a.H * E;
+  da.base = a.hidden + (size_t)h0 * E;
+  da.ld_bytes = ldh;
+  da.nrec = a.N > 0 ? (uint32_t)((size_t)a.N * ldh - (size_t)h0 * E) : 0u;
+  da.cols_valid = a.H - h0;
+  da.k_bytes = 0;
+  const uint32_t ldd = (uint32_t)a.ldD * E;
+  db.base = a.D + (size_t)vl0 * E;
+  db.ld_bytes = ldd;
+  db.nrec = a.N_pad > 0 ? (uint32_t)((size_t)a.N_pad * ldd - (size_t)vl0 * E) : 0u;
+  db.cols_valid = a.ldD - vl0;
+  db.k_bytes = 0;
+  constexpr int kRowsPerStage = kBKB / E;
+  const int KT = (a.N + kRowsPerStage - 1) / kRowsPerStage;
+
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  tile_mainloop<T, false, false>(da, db, KT, acc);
+
+#pragma unroll
+  for (int ni = 0; ni < 4; ni++) {
+    const int v = a.cv0 + vl0 + wn * 128 + ni * 32 + (lane & 31);
+    if (v >= a.V) continue;
+#pragma unroll
+    for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const int h = h0 + wm * 128 + mi * 32 + 8 * g + 4 * (lane >> 5);
+        if (h >= a.H) continue;
+        const size_t o = (size_t)v * a.H + h;
+        if (a.gw_f32)
+          store4(reinterpret_cast<float*>(a.gw) + o, acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1],
+                 acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
+        else
+          store4(reinterpret_cast<bf16*>(a.gw) + o, acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1],
+                 acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// grad_hidden for one chunk: C[h][t] = sum_v weight[v][h] D[t][v]
+// A = weight (MNMAJOR: rows v, cols h), B = D (KMAJOR: rows t, K = v).
+// mode 0: first of several chunks (store fp32 accumulator)
+// mode 1: middle chunk (accumulator += C)
+// mode 2: last chunk (out = cast(accumulator + C))
+// mode 3: only chunk (out = cast(C))
+// ---------------------------------------------------------------------------
+struct GhArgs {
+  const char* weight;
+  const char* D;
+  int ldD;
+  int N, H, V;
+  int cv0, cvn;     // chunk start and padded width
+  int n_ht, n_tt;
+  float* accb;      // fp32 N x H accumulator (may alias out when out is fp32)
+  void* out;
+  int out_f32;
+  int mode;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void bwd_gh_kernel(GhArgs a) {
+  constexpr int E = sizeof(T);
+  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  int ht, tt;
+  grouped_tile(L, a.n_ht, a.n_tt, 4, ht, tt);
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h0 = ht * 256, t0 = tt * 256;
+
+  OperandDesc da, db;
+  const uint32_t ldw = (uint32_t)a.H * E;
+  const int vrows = min(a.V - a.cv0, a.cvn);
+  da.base = a.weight + ((size_t)a.cv0 * a.H + h0) * E;
+  da.ld_bytes = ldw;
+  da.nrec = (uint32_t)((size_t)vrows * ldw - (size_t)h0 * E);
+  da.cols_valid = a.H - h0;
+  da.k_bytes = 0;
+  const uint32_t ldd = (uint32_t)a.ldD * E;
+  db.base = a.D + (size_t)t0 * ldd;
+  db.ld_bytes = ldd;
+  db.nrec = 256u * ldd;
+  db.cols_valid = 0;
+  db.k_bytes = a.cvn * E;
+  const int KT = (a.cvn * E + kBKB - 1) / kBKB;
+
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  tile_mainloop<T, false, true>(da, db, KT, acc);
+
+#pragma unroll
+  for (int ni = 0; ni < 4; ni++) {
+    const int t = t0 + wn * 128 + ni * 32 + (lane & 31);
+    if (t >= a.N) continue;
+#pragma unroll
+    for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const int h = h0 + wm * 128 + mi * 32 + 8 * g + 4 * (lane >> 5);
+        if (h >= a.H) continue;
+        const size_t o = (size_t)t * a.H + h;
+        float c0 = acc[mi][ni][4 * g], c1 = acc[mi][ni][4 * g + 1];
+        float c2 = acc[mi][ni][4 * g + 2], c3 = acc[mi][ni][4 * g + 3];
+        if (a.mode == 1 || a.mode == 2) {
+          const f32x4 prev = *reinterpret_cast<const f32x4*>(a.accb + o);
+          c0 += prev[0];
+          c1 += prev[1];
+          c2 += prev[2];
+          c3 += prev[3];
+        }
+        if (a.mode <= 1 || a.out_f32) {
+          float* dst = (a.mode <= 1) ? a.accb + o : reinterpret_cast<float*>(a.out) + o;
+          store4(dst, c0, c1, c2, c3);
+        } else {
+          store4(reinterpret_cast<bf16*>(a.out) + o, c0, c1, c2, c3);
+        }
+      }
+  }
+}
+
+// grad_bias[v] = sum over token tiles of the per-tile column sums, in order.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_gb_reduce(const float* part, int n_tt, int ld, int V, T* gb) {
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  if (v >= V) return;
+  float s = 0.0f;
+  for (int i = 0; i < n_tt; i++) s += part[(size_t)i * ld + v];
+  gb[v] = (T)s;
+}
+
+template <typename T>
+static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const void* weight,
+                                    const void* bias, const int64_t* targets, const float* lse,
+                                    const float* grad_loss, void* grad_hidden, void* grad_weight,
+                                    void* grad_bias, char* ws, hipStream_t st) {
+  float* coefA = reinterpret_cast<float*>(ws + pl.b_coefA);
+  float* coefB = reinterpret_cast<float*>(ws + pl.b_coefB);
+  float* lseL = reinterpret_cast<float*>(ws + pl.b_lseL);
+  int* tgt = reinterpret_cast<int*>(ws + pl.b_tgt);
+  char* D = ws + pl.b_D;
+  float* gb_part = reinterpret_cast<float*>(ws + pl.b_gbpart);
+
+  PrepArgs pa;
+  pa.targets = targets;
+  pa.lse = lse;
+  pa.grad_loss = grad_loss;
+  pa.N = (int)pl.N;
+  pa.V = (int)pl.V;
+  pa.N_pad = (int)pl.N_pad;
+  pa.reduction = pl.reduction;
+  pa.ignore_index = pl.ignore_index;
+  pa.z_loss = pl.z_loss;
+  pa.coefA = coefA;
+  pa.coefB = coefB;
+  pa.lseL = lseL;
+  pa.tgt = tgt;
+  pa.status = reinterpret_cast<int*>(ws);
+  bwd_prep_kernel<<<1, 1024, 0, st>>>(pa);
+
+  const bool gh_f32 = pl.dtype == FLCE_F32;
+  float* accb = gh_f32 ? reinterpret_cast<float*>(grad_hidden) : reinterpret_cast<float*>(ws + pl.b_ghacc);
+  const int ldD = (int)pl.Vc;
+
+  for (int c = 0; c < pl.n_chunks; c++) {
+    const int cv0 = (int)(c * pl.Vc);
+    const int cvn = (int)(pl.V_pad - cv0 < pl.Vc ? pl.V_pad - cv0 : pl.Vc);
+    const int n_vt_c = cvn / 256;
+    if (pl.N > 0) {
+      DlogitsArgs d;
+      d.hidden = static_cast<const char*>(hidden);
+      d.weight = static_cast<const char*>(weight);
+      d.bias = bias;
+      d.N = (int)pl.N;
+      d.H = (int)pl.H;
+      d.V = (int)pl.V;
+      d.scale = pl.scale;
+      d.cap = pl.cap;
+      d.two_log2e_over_cap = pl.cap > 0 ? 2.0f * kLog2e / pl.cap : 0.0f;
+      d.two_cap = 2.0f * pl.cap;
+      d.neg_scale_over_cap2 = pl.cap > 0 ? -pl.scale / (pl.cap * pl.cap) : 0.0f;
+      d.cv0 = cv0;
+      d.n_vt_c = n_vt_c;
+      d.n_tt = (int)pl.n_tt;
+      d.coefA = coefA;
+      d.coefB = coefB;
+      d.lseL = lseL;
+      d.tgt = tgt;
+      d.D = D;
+      d.ldD = ldD;
+      d.gb_part = gb_part;
+      d.ld_gb = (int)pl.V_pad;
+      const int nwg = n_vt_c * (int)pl.n_tt;
+      if (pl.has_bias) {
+        if (pl.cap > 0) bwd_dlogits_kernel<T, true, true><<<nwg, 256, 0, st>>>(d);
+        else bwd_dlogits_kernel<T, true, false><<<nwg, 256, 0, st>>>(d);
+      } else {
+        if (pl.cap > 0) bwd_dlogits_kernel<T, false, true><<<nwg, 256, 0, st>>>(d);
+        else bwd_dlogits_kernel<T, false, false><<<nwg, 256, 0, st>>>(d);
+      }
+    }
+    {
+      GwArgs g;
+      g.hidden = static_cast<const char*>(hidden);
+      g.D = D;
+      g.ldD = ldD;
+      g.N = (int)pl.N;
+      g.H = (int)pl.H;
+      g.V = (int)pl.V;
+      g.N_pad = (int)pl.N_pad;
+      g.cv0 = cv0;
+      g.n_ht = (int)pl.n_ht;
+      g.n_vt_c = n_vt_c;
+      g.gw = grad_weight;
+      g.gw_f32 = pl.gw_dtype == FLCE_F32;
+      bwd_gw_kernel<T><<<(int)pl.n_ht * n_vt_c, 256, 0, st>>>(g);
+    }
+    if (pl.N > 0) {
+      GhArgs h;
+      h.weight = static_cast<const char*>(weight);
+      h.D = D;
+      h.ldD = ldD;
+      h.N = (int)pl.N;
+      h.H = (int)pl.H;
+      h.V = (int)pl.V;
+      h.cv0 = cv0;
+      h.cvn = cvn;
+      h.n_ht = (int)pl.n_ht;
+      h.n_tt = (int)pl.n_tt;
+      h.accb = accb;
+      h.out = grad_hidden;
+      h.out_f32 = gh_f32;
+      h.mode = pl.n_chunks == 1 ? 3 : (c == 0 ? 0 : (c == pl.n_chunks - 1 ? 2 : 1));
+      bwd_gh_kernel<T><<<(int)(pl.n_ht * pl.n_tt), 256, 0, st>>>(h);
+    }
+  }
+  if (grad_bias) {
+    bwd_gb_reduce<T><<<(int)((pl.V + 255) / 256), 256, 0, st>>>(gb_part, (int)pl.n_tt, (int)pl.V_pad,
+                                                               (int)pl.V, reinterpret_cast<T*>(grad_bias));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
+                           const int64_t* targets, const float* lse, const float* grad_loss,
+                           void* grad_hidden, void* grad_weight, void* grad_bias, char* ws,
+                           hipStream_t st) {
+  if (pl.dtype == FLCE_BF16)
+    return launch_backward_t<bf16>(pl, hidden, weight, bias, targets, lse, grad_loss, grad_hidden,
+                                   grad_weight, grad_bias, ws, st);
+  return launch_backward_t<float>(pl, hidden, weight, bias, targets, lse, grad_loss, grad_hidden,
+                                  grad_weight, grad_bias, ws, st);
+}
+
+}  // namespace flce

@@ -1,0 +1,437 @@
+// Forward pass: vocabulary-tiled logit GEMM with an online-softmax epilogue,
+// then a fixed-order merge of the vocabulary splits and of the scalar sums.
+//
+// Method: fused-linear-ce README, "Algorithm" (tile over the vocabulary,
+// fp32 accumulator, bias / logit_scale / softcap, online log-sum-exp merge,
+// nothing of size (N, V) written) and "Metrics for free" (argmax carried with
+// the running max; sum_j p_j z_j carried with the same rescaling).
+#include "flce_device.h"
+#include "flce_internal.h"
+
+namespace flce {
+
+struct FwdTileArgs {
+  const char* hidden;
+  const char* weight;
+  const void* bias;
+  const int64_t* targets;
+  int N, H, V;
+  int64_t ignore_index;
+  float scale, cap, two_log2e_over_cap, two_cap;
+  int n_vt, S, N_pad;
+  float* part_m;
+  float* part_l;
+  float* part_T;
+  int* part_idx;
+  float* part_zt;
+};
+
+// Per-lane running softmax state for one token column.
+struct RowState {
+  float m, l, T, zt;
+  int idx;
+};
+
+__device__ __forceinline__ void merge_state(RowState& a, const RowState& b) {
+  const float mn = fmaxf(a.m, b.m);
+  const float fa = fast_exp2((a.m - mn) * kLog2e);
+  const float fb = fast_exp2((b.m - mn) * kLog2e);
+  a.l = a.l * fa + b.l * fb;
+  a.T = a.T * fa + b.T * fb;
+  a.idx = b.m > a.m ? b.idx : (a.m > b.m ? a.idx : min(a.idx, b.idx));
+  a.m = mn;
+  a.zt = fmaxf(a.zt, b.zt);
+}
+
+// Loads 4 consecutive bias entries starting at row `r0`, zero past V.
+template <typename T>
+__device__ __forceinline__ void load_bias4(const T* b, int r0, int V, float* out) {
+  if (r0 + 3 < V) {
+    if constexpr (sizeof(T) == 2) {
+      const bf16x4 v = *reinterpret_cast<const bf16x4*>(b + r0);
+#pragma unroll
+      for (int j = 0; j < 4; j++) out[j] = (float)v[j];
+    } else {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(b + r0);
+#pragma unroll
+      for (int j = 0; j < 4; j++) out[j] = v[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; j++) out[j] = (r0 + j < V) ? load_elem<T>(b, r0 + j) : 0.0f;
+  }
+}
+
+template <typename T, bool HAS_BIAS, bool SOFTCAP>
+__global__ __launch_bounds__(256, 1) void fwd_tiles_kernel(FwdTileArgs a) {
+  constexpr int E = sizeof(T);
+  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int tt = L / a.S, s = L % a.S;
+  const int vt_begin = (int)((int64_t)s * a.n_vt / a.S);
+  const int vt_end = (int)((int64_t)(s + 1) * a.n_vt / a.S);
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = tt * 256;
+
+  int tgt[4];
+  RowState st[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ni++) {
+    const int t = t0 + wn * 128 + ni * 32 + (lane & 31);
+    const int64_t tv = t < a.N ? a.targets[t] : a.ignore_index;
+    tgt[ni] = (tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1;
+    st[ni].m = kMasked;
+    st[ni].l = 0.0f;
+    st[ni].T = 0.0f;
+    st[ni].zt = -INFINITY;
+    st[ni].idx = 0;
+  }
+
+  const uint32_t ld = (uint32_t)a.H * E;
+  OperandDesc db;
+  db.base = a.hidden + (size_t)t0 * ld;
+  db.ld_bytes = ld;
+  db.nrec = (uint32_t)min(a.N - t0, 256) * ld;
+  db.cols_valid = 0;
+  db.k_bytes = a.H * E;
+  const int KT = (a.H * E + kBKB - 1) / kBKB;
+
+  f32x16 acc[4][4];
+  for (int vt = vt_begin; vt < vt_end; ++vt) {
+    const int v0 = vt * 256;
+    OperandDesc da;
+    da.base = a.weight + (size_t)v0 * ld;
+    da.ld_bytes = ld;
+    da.nrec = (uint32_t)min(a.V - v0, 256) * ld;
+    da.cols_valid = 0;
+    da.k_bytes = a.H * E;
+    zero_acc(acc);
+    tile_mainloop<T, true, true>(da, db, KT, acc);
+
+    // ---- epilogue: transform each 32-row MFMA tile and merge it into the
+    // running state of its token column (rows visited in ascending order, so
+    // a strict > keeps the lowest index on ties)
+    const int vw = v0 + wm * 128;
+    const bool ragged = vw + 128 > a.V;
+#pragma unroll
+    for (int mi = 0; mi < 4; mi++) {
+      float sb[16];
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        float b4[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (HAS_BIAS)
+          load_bias4<T>(reinterpret_cast<const T*>(a.bias), vw + mi * 32 + 8 * g + 4 * (lane >> 5), a.V, b4);
+#pragma unroll
+        for (int j = 0; j < 4; j++) sb[4 * g + j] = a.scale * b4[j];
+      }
+#pragma unroll
+      for (int ni = 0; ni < 4; ni++) {
+        float z[16];
+        float mx = kMasked;
+        int ix = 0;
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          float v = HAS_BIAS ? fmaf(acc[mi][ni][r], a.scale, sb[r]) : acc[mi][ni][r] * a.scale;
+          if constexpr (SOFTCAP) v = softcap_apply(v, a.two_log2e_over_cap, a.cap, a.two_cap);
+          const int row = acc_row(mi, r, lane);
+          if (ragged && vw + row >= a.V) v = kMasked;
+          z[r] = v;
+          if (v > mx) {
+            mx = v;
+            ix = row;
+          }
+        }
+        // the target logit, where some lane of the wave holds its row here
+        const int rel = tgt[ni] - vw - mi * 32;
+        const bool hit = rel >= 0 && rel < 32 && (((rel >> 2) & 1) == (lane >> 5));
+        if (__builtin_amdgcn_ballot_w64(hit)) {
+#pragma unroll
+          for (int r = 0; r < 16; r++)
+            if (acc_row(0, r, lane) == rel) st[ni].zt = z[r];
+        }
+        const float m_old = st[ni].m;
+        const float m_new = fmaxf(m_old, mx);
+        if (mx > m_old) st[ni].idx = vw + ix;
+        const float mL = m_new * kLog2e;
+        const float alpha = fast_exp2(fmaf(m_old, kLog2e, -mL));
+        float se0 = 0.f, se1 = 0.f, sz0 = 0.f, sz1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float e0 = fast_exp2(fmaf(z[r], kLog2e, -mL));
+          const float e1 = fast_exp2(fmaf(z[r + 1], kLog2e, -mL));
+          se0 += e0;
+          se1 += e1;
+          sz0 = fmaf(e0, z[r], sz0);
+          sz1 = fmaf(e1, z[r + 1], sz1);
+        }
+        st[ni].l = fmaf(st[ni].l, alpha, se0 + se1);
+        st[ni].T = fmaf(st[ni].T, alpha, sz0 + sz1);
+        st[ni].m = m_new;
+      }
+    }
+  }
+
+  // ---- merge the two lane halves (same tokens, interleaved rows)
+#pragma unroll
+  for (int ni = 0; ni < 4; ni++) {
+    RowState o;
+    o.m = __shfl_xor(st[ni].m, 32);
+    o.l = __shfl_xor(st[ni].l, 32);
+    o.T = __shfl_xor(st[ni].T, 32);
+    o.zt = __shfl_xor(st[ni].zt, 32);
+    o.idx = __shfl_xor(st[ni].idx, 32);
+    merge_state(st[ni], o);
+  }
+  // ---- merge the two M waves through LDS, then write the split's partials
+  float* xs = reinterpret_cast<float*>(g_stage0);   // [wn][field][128]
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ni++) {
+      const int c = ni * 32 + lane;
+      float* p = xs + wn * 5 * 128;
+      p[0 * 128 + c] = st[ni].m;
+      p[1 * 128 + c] = st[ni].l;
+      p[2 * 128 + c] = st[ni].T;
+      p[3 * 128 + c] = st[ni].zt;
+      p[4 * 128 + c] = __int_as_float(st[ni].idx);
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ni++) {
+      const int c = ni * 32 + lane;
+      const float* p = xs + wn * 5 * 128;
+      RowState o;
+      o.m = p[0 * 128 + c];
+      o.l = p[1 * 128 + c];
+      o.T = p[2 * 128 + c];
+      o.zt = p[3 * 128 + c];
+      o.idx = __float_as_int(p[4 * 128 + c]);
+      merge_state(st[ni], o);
+      const int t = t0 + wn * 128 + c;
+      const size_t o_ = (size_t)s * a.N_pad + t;
+      a.part_m[o_] = st[ni].m;
+      a.part_l[o_] = st[ni].l;
+      a.part_T[o_] = st[ni].T;
+      a.part_zt[o_] = st[ni].zt;
+      a.part_idx[o_] = st[ni].idx;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Finalize: merge the S splits of each row in order, then per-block sums.
+// ---------------------------------------------------------------------------
+struct FinArgs {
+  const int64_t* targets;
+  int N, V, S, N_pad, reduction;
+  int64_t ignore_index;
+  float z_loss;
+  const float* part_m;
+  const float* part_l;
+  const float* part_T;
+  const int* part_idx;
+  const float* part_zt;
+  float* loss;
+  float* lse;
+  BlockPart* blk;
+};
+
+__global__ __launch_bounds__(256) void fwd_finalize_rows(FinArgs a) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  double lsum = 0.0, esum = 0.0;
+  int nv = 0, nc = 0, bad = 0;
+  if (i < a.N) {
+    RowState r;
+    r.m = a.part_m[i];
+    r.l = a.part_l[i];
+    r.T = a.part_T[i];
+    r.zt = a.part_zt[i];
+    r.idx = a.part_idx[i];
+    for (int s = 1; s < a.S; s++) {
+      const size_t o = (size_t)s * a.N_pad + i;
+      RowState q;
+      q.m = a.part_m[o];
+      q.l = a.part_l[o];
+      q.T = a.part_T[o];
+      q.zt = a.part_zt[o];
+      q.idx = a.part_idx[o];
+      merge_state(r, q);
+    }
+    const float lse = r.m + fast_log2(r.l) * kLn2;
+    const float ent = lse - r.T / r.l;
+    const int64_t t = a.targets[i];
+    const bool in_range = t >= 0 && t < a.V;
+    const bool valid = t != a.ignore_index && in_range;
+    bad = (t != a.ignore_index && !in_range) ? 1 : 0;
+    const float row_loss = valid ? (lse - r.zt + a.z_loss * lse * lse) : 0.0f;
+    a.lse[i] = lse;
+    if (a.reduction == FLCE_REDUCTION_NONE) a.loss[i] = row_loss;
+    lsum = row_loss;
+    esum = valid ? (double)ent : 0.0;
+    nv = valid ? 1 : 0;
+    nc = (valid && r.idx == (int)t) ? 1 : 0;
+  }
+  __shared__ double sl[256], se[256];
+  __shared__ int sv[256], sc[256], sb[256];
+  const int tid = threadIdx.x;
+  sl[tid] = lsum;
+  se[tid] = esum;
+  sv[tid] = nv;
+  sc[tid] = nc;
+  sb[tid] = bad;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+      sl[tid] += sl[tid + w];
+      se[tid] += se[tid + w];
+      sv[tid] += sv[tid + w];
+      sc[tid] += sc[tid + w];
+      sb[tid] |= sb[tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    BlockPart b;
+    b.loss = sl[0];
+    b.entropy = se[0];
+    b.n_valid = sv[0];
+    b.n_correct = sc[0];
+    b.bad_target = sb[0];
+    b.pad = 0;
+    a.blk[blockIdx.x] = b;
+  }
+}
+
+struct ScalarArgs {
+  const BlockPart* blk;
+  int nblk, reduction;
+  float* loss;
+  int64_t* num_correct;
+  float* entropy_sum;
+  int* status;
+};
+
+__global__ __launch_bounds__(256) void fwd_finalize_scalars(ScalarArgs a) {
+  __shared__ double sl[256], se[256];
+  __shared__ long long sv[256], sc[256];
+  __shared__ int sb[256];
+  const int tid = threadIdx.x;
+  double l = 0.0, e = 0.0;
+  long long v = 0, c = 0;
+  int b = 0;
+  for (int j = tid; j < a.nblk; j += 256) {
+    const BlockPart p = a.blk[j];
+    l += p.loss;
+    e += p.entropy;
+    v += p.n_valid;
+    c += p.n_correct;
+    b |= p.bad_target;
+  }
+  sl[tid] = l;
+  se[tid] = e;
+  sv[tid] = v;
+  sc[tid] = c;
+  sb[tid] = b;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+      sl[tid] += sl[tid + w];
+      se[tid] += se[tid + w];
+      sv[tid] += sv[tid + w];
+      sc[tid] += sc[tid + w];
+      sb[tid] |= sb[tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (a.reduction == FLCE_REDUCTION_SUM) a.loss[0] = (float)sl[0];
+    else if (a.reduction == FLCE_REDUCTION_MEAN)
+      a.loss[0] = sv[0] > 0 ? (float)(sl[0] / (double)sv[0]) : __builtin_nanf("");
+    if (a.num_correct) a.num_correct[0] = (int64_t)sc[0];
+    if (a.entropy_sum) a.entropy_sum[0] = (float)se[0];
+    a.status[0] = sb[0] ? FLCE_ERR_TARGET_OUT_OF_RANGE : FLCE_OK;
+  }
+}
+
+template <typename T>
+static void launch_fwd_tiles(const Plan& pl, const FwdTileArgs& args, int nwg, hipStream_t st) {
+  if (pl.has_bias) {
+    if (pl.cap > 0) fwd_tiles_kernel<T, true, true><<<nwg, 256, 0, st>>>(args);
+    else fwd_tiles_kernel<T, true, false><<<nwg, 256, 0, st>>>(args);
+  } else {
+    if (pl.cap > 0) fwd_tiles_kernel<T, false, true><<<nwg, 256, 0, st>>>(args);
+    else fwd_tiles_kernel<T, false, false><<<nwg, 256, 0, st>>>(args);
+  }
+}
+
+hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
+                          const int64_t* targets, float* loss, float* lse, int64_t* num_correct,
+                          float* entropy_sum, char* ws, hipStream_t st) {
+  const size_t NP = (size_t)pl.N_pad * pl.S;
+  float* part_m = reinterpret_cast<float*>(ws + pl.f_part);
+  float* part_l = part_m + NP;
+  float* part_T = part_l + NP;
+  float* part_zt = part_T + NP;
+  int* part_idx = reinterpret_cast<int*>(part_zt + NP);
+  BlockPart* blk = reinterpret_cast<BlockPart*>(ws + pl.f_blk);
+
+  if (pl.N > 0) {
+    FwdTileArgs a;
+    a.hidden = static_cast<const char*>(hidden);
+    a.weight = static_cast<const char*>(weight);
+    a.bias = bias;
+    a.targets = targets;
+    a.N = (int)pl.N;
+    a.H = (int)pl.H;
+    a.V = (int)pl.V;
+    a.ignore_index = pl.ignore_index;
+    a.scale = pl.scale;
+    a.cap = pl.cap;
+    a.two_log2e_over_cap = pl.cap > 0 ? 2.0f * kLog2e / pl.cap : 0.0f;
+    a.two_cap = 2.0f * pl.cap;
+    a.n_vt = (int)pl.n_vt;
+    a.S = pl.S;
+    a.N_pad = (int)pl.N_pad;
+    a.part_m = part_m;
+    a.part_l = part_l;
+    a.part_T = part_T;
+    a.part_idx = part_idx;
+    a.part_zt = part_zt;
+    const int nwg = (int)(pl.n_tt * pl.S);
+    if (pl.dtype == FLCE_BF16) launch_fwd_tiles<bf16>(pl, a, nwg, st);
+    else launch_fwd_tiles<float>(pl, a, nwg, st);
+  }
+  const int nblk = (int)((pl.N + 255) / 256) > 0 ? (int)((pl.N + 255) / 256) : 1;
+  FinArgs f;
+  f.targets = targets;
+  f.N = (int)pl.N;
+  f.V = (int)pl.V;
+  f.S = pl.S;
+  f.N_pad = (int)pl.N_pad;
+  f.reduction = pl.reduction;
+  f.ignore_index = pl.ignore_index;
+  f.z_loss = pl.z_loss;
+  f.part_m = part_m;
+  f.part_l = part_l;
+  f.part_T = part_T;
+  f.part_idx = part_idx;
+  f.part_zt = part_zt;
+  f.loss = loss;
+  f.lse = lse;
+  f.blk = blk;
+  fwd_finalize_rows<<<nblk, 256, 0, st>>>(f);
+  ScalarArgs sa;
+  sa.blk = blk;
+  sa.nblk = nblk;
+  sa.reduction = pl.reduction;
+  sa.loss = loss;
+  sa.num_correct = num_correct;
+  sa.entropy_sum = entropy_sum;
+  sa.status = reinterpret_cast<int*>(ws);
+  fwd_finalize_scalars<<<1, 256, 0, st>>>(sa);
+  return hipGetLastError();
+}
+
+}  // namespace flce

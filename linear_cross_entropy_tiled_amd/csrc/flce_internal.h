@@ -1,0 +1,56 @@
+// Host-side plan, workspace layout and kernel launchers (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/flce.h"
+
+namespace flce {
+
+// Everything the launchers need, derived from flce_params on the host.
+struct Plan {
+  int64_t N, H, V, ignore_index;
+  int dtype, gw_dtype, reduction;
+  bool has_bias;
+  float scale, cap, z_loss;
+
+  int64_t n_tt, n_vt, n_ht;      // 256-wide tiles over tokens, vocabulary, hidden
+  int64_t N_pad, V_pad;          // padded to whole tiles
+  int esize;                     // bytes per input element
+
+  // forward
+  int S;                         // vocabulary splits per token tile
+  size_t f_part, f_blk, f_bytes; // workspace offsets / total
+
+  // backward
+  int64_t Vc;                    // vocabulary chunk width (multiple of 256)
+  int n_chunks;
+  size_t b_coefA, b_coefB, b_lseL, b_tgt, b_D, b_ghacc, b_gbpart, b_bytes;
+};
+
+constexpr size_t kStatusBytes = 256;   // status word at workspace offset 0
+
+// Partial sums of one finalize block (forward).
+struct BlockPart {
+  double loss;
+  double entropy;
+  int n_valid;
+  int n_correct;
+  int bad_target;
+  int pad;
+};
+
+int make_plan(const flce_params* p, Plan* plan);
+
+hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
+                          const int64_t* targets, float* loss, float* lse, int64_t* num_correct,
+                          float* entropy_sum, char* ws, hipStream_t st);
+
+hipError_t launch_backward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
+                           const int64_t* targets, const float* lse, const float* grad_loss,
+                           void* grad_hidden, void* grad_weight, void* grad_bias, char* ws,
+                           hipStream_t st);
+
+}  // namespace flce

@@ -1,0 +1,105 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/flce.h declares, sizes workspaces, and rejects bad arguments on the
+host before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_cross_entropy_tiled_amd as flce
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "flce.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(flce.LIB_PATH):
+        from linear_cross_entropy_tiled_amd import build
+        build.build()
+    return flce.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(flce_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(flce.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert flce.flce_version() >= 100
+    assert flce.flce_status_string(flce.FLCE_ERR_WORKSPACE_TOO_SMALL) == "workspace too small"
+
+
+def test_struct_layout_matches_header():
+    # 4 x int64, 4 x int32, 4 x float
+    assert ctypes.sizeof(flce.flce_params) == 64
+    assert flce.flce_params.dtype.offset == 32 and flce.flce_params.logit_scale.offset == 48
+
+
+def _ws(p, pass_):
+    out = ctypes.c_size_t(0)
+    rc = flce.load().flce_workspace_size(ctypes.byref(p), pass_, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_workspace_sizes(lib):
+    p = flce.make_params(8192, 4096, 128256, dtype="bf16", reduction="sum", softcap=30.0)
+    rc, fb = _ws(p, flce.FLCE_PASS_FORWARD)
+    assert rc == 0 and 0 < fb < 64 << 20
+    rc, bb = _ws(p, flce.FLCE_PASS_BACKWARD)
+    # dlogits chunk scratch + fp32 grad_hidden accumulator + grad_bias partials:
+    # O(N*H + N*Vc + V), far below the N*V bf16 logits (2.1 GB)
+    assert rc == 0 and bb < 1.2e9
+    p0 = flce.make_params(0, 64, 10)
+    assert _ws(p0, flce.FLCE_PASS_FORWARD)[0] == 0
+    assert _ws(p0, flce.FLCE_PASS_BACKWARD)[0] == 0
+    assert _ws(p, 7)[0] == flce.FLCE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("hidden", 100, flce.FLCE_ERR_UNSUPPORTED),          # H % 8 != 0
+    ("hidden", 0, flce.FLCE_ERR_INVALID_ARG),
+    ("vocab", 0, flce.FLCE_ERR_INVALID_ARG),
+    ("n_tokens", -1, flce.FLCE_ERR_INVALID_ARG),
+    ("dtype", 7, flce.FLCE_ERR_INVALID_ARG),
+    ("grad_weight_dtype", 9, flce.FLCE_ERR_INVALID_ARG),
+    ("reduction", 3, flce.FLCE_ERR_INVALID_ARG),
+    ("reserved", 1, flce.FLCE_ERR_INVALID_ARG),
+    ("z_loss", -1.0, flce.FLCE_ERR_INVALID_ARG),
+    ("logit_scale", float("inf"), flce.FLCE_ERR_INVALID_ARG),
+])
+def test_bad_params_rejected(lib, field, value, code):
+    p = flce.make_params(64, 64, 100)
+    setattr(p, field, value)
+    assert _ws(p, flce.FLCE_PASS_FORWARD)[0] == code
+    rc = lib.flce_forward(ctypes.byref(p), 16, 16, None, 16, 16, 16, None, None, 16, 1 << 30, None)
+    assert rc == code
+
+
+def test_null_and_misaligned_pointers_rejected(lib):
+    p = flce.make_params(64, 64, 100)
+    big = 1 << 30
+    # NULL loss / lse / workspace / weight
+    assert lib.flce_forward(ctypes.byref(p), 16, 16, None, 16, None, 16, None, None, 16, big, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_forward(ctypes.byref(p), 16, None, None, 16, 16, 16, None, None, 16, big, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_forward(ctypes.byref(p), 16, 16, None, 16, 16, 16, None, None, None, big, None) == flce.FLCE_ERR_INVALID_ARG
+    # hidden not 16-byte aligned
+    assert lib.flce_forward(ctypes.byref(p), 18, 16, None, 16, 16, 16, None, None, 16, big, None) == flce.FLCE_ERR_UNSUPPORTED
+    # workspace too small
+    assert lib.flce_forward(ctypes.byref(p), 16, 16, None, 16, 16, 16, None, None, 16, 8, None) == flce.FLCE_ERR_WORKSPACE_TOO_SMALL
+    # backward: grad_bias without bias, missing grad_weight
+    assert lib.flce_backward(ctypes.byref(p), 16, 16, None, 16, 16, 16, 16, 16, 16, 16, big, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_backward(ctypes.byref(p), 16, 16, None, 16, 16, 16, 16, None, None, 16, big, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_backward(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 8, None) == flce.FLCE_ERR_WORKSPACE_TOO_SMALL
+    assert lib.flce_get_status(None, None) == flce.FLCE_ERR_INVALID_ARG
+
+
+def test_too_large_problem_rejected(lib):
+    p = flce.make_params(1 << 20, 4096, 1000)       # N*H*2 bytes >= 2 GiB
+    assert _ws(p, flce.FLCE_PASS_FORWARD)[0] == flce.FLCE_ERR_UNSUPPORTED

@@ -1,0 +1,297 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Small and medium cases compare every output element; the full-size workloads
+compare sampled gradient rows with the oracle's LSE computed for every row.
+Tolerances: loss, LSE and entropy relative 2e-3 (bf16) / 1e-5 (fp32);
+gradients max |err| <= 1e-2 * max |ref|; num_correct exact except for rows
+whose two largest oracle logits are closer than 1e-3.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs as si
+from gpu_helpers import (assert_grad_close, assert_loss_close, assert_num_correct, t2np, to_device,
+                         widened)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+@dataclasses.dataclass
+class Case:
+    name: str
+    n: int
+    h: int
+    v: int
+    dtype: str = "bf16"
+    bias_std: float = None
+    scale: float = 1.0
+    cap: float = None
+    z_loss: float = 0.0
+    ignore_frac: float = 0.0
+    reduction: str = "mean"
+    gw_dtype: str = None
+    targets: str = "uniform"
+    weight_std: float = 0.02
+    seed: int = 11
+
+
+def _from_workload(wl: si.Workload) -> Case:
+    return Case(wl.name, wl.n_tokens, wl.hidden, wl.vocab, wl.dtype, wl.bias_std, wl.logit_scale,
+                wl.softcap, wl.z_loss, wl.ignore_frac, wl.reduction, wl.grad_weight_dtype, wl.targets,
+                wl.weight_std, wl.seed)
+
+
+SMALL_CASES = [
+    _from_workload(si.WORKLOADS["tiny_fp32"]),
+    _from_workload(si.WORKLOADS["bf16_n2048_h1024_v32000"]),
+    # several tiles in every dimension, ragged tails (N, V not multiples of 256,
+    # H not a multiple of the 64-wide K stage), every option on
+    Case("ragged_bf16_all_options", 700, 200, 1500, "bf16", 0.1, 0.7, 2.0, 0.01, 0.1, "mean",
+         weight_std=0.1),
+    Case("ragged_bf16_none_gwf32", 333, 136, 777, "bf16", None, 1.0, None, 0.0, 0.05, "none", "f32",
+         weight_std=0.1),
+    Case("ragged_f32_sum_softcap", 300, 72, 1000, "f32", 0.2, 0.5, 5.0, 0.001, 0.0, "sum",
+         weight_std=0.1),
+    Case("vocab_smaller_than_tile", 513, 64, 37, "bf16", 0.1, 1.0, None, 0.0, 0.0, "sum",
+         weight_std=0.2),
+    Case("single_row", 1, 128, 300, "bf16", 0.1, 1.3, 10.0, 0.0, 0.0, "mean", weight_std=0.1),
+    # more than one vocabulary chunk in the backward pass (chunk <= 32768 rows)
+    Case("two_vocab_chunks_bias", 256, 64, 40000, "bf16", 0.1, 1.0, None, 1e-3, 0.1, "mean",
+         weight_std=0.1),
+    Case("zipf_targets_zloss", 1024, 256, 5000, "bf16", None, 1.0, None, 1e-4, 0.0, "mean",
+         targets="zipf", weight_std=0.05),
+]
+
+
+def _inputs(c: Case):
+    return si.make_inputs(c.n, c.h, c.v, dtype=c.dtype, weight_std=c.weight_std, bias_std=c.bias_std,
+                          targets=c.targets, ignore_frac=c.ignore_frac, reduction=c.reduction,
+                          seed=c.seed)
+
+
+def _opts(c: Case):
+    return dict(logit_scale=c.scale, softcap=c.cap, z_loss=c.z_loss, reduction=c.reduction)
+
+
+def _run_gpu(flce, c: Case, d: dict, return_metrics=True):
+    import torch
+    loss, lse, met = flce.forward(d["hidden"], d["weight"], d["targets"], d["bias"],
+                                  return_metrics=return_metrics, **_opts(c))
+    g = d["grad_loss"] if c.reduction == "none" else d["grad_loss"][:1]
+    gh, gw, gb = flce.backward(d["hidden"], d["weight"], d["targets"], lse, g, d["bias"],
+                               grad_weight_dtype=c.gw_dtype, **_opts(c))
+    torch.cuda.synchronize()
+    return loss, lse, met, gh, gw, gb
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: c.name)
+def test_full_parity(flce_lib, case):
+    c = case
+    _say(f"[parity] {c.name} N={c.n} H={c.h} V={c.v} {c.dtype} {c.reduction}")
+    inp = _inputs(c)
+    d = to_device(inp, c.dtype)
+    loss, lse, met, gh, gw, gb = _run_gpu(flce_lib, c, d)
+    X, W, B, T = widened(inp, c.dtype)
+    fwd, rgh, rgw, rgb = oracle.forward_backward(X, W, B, T, inp["grad_loss"].astype(np.float64),
+                                                 **_opts(c))
+    assert_loss_close(t2np(loss), fwd.loss, c.dtype, "loss")
+    assert_loss_close(t2np(lse), fwd.lse, c.dtype, "lse")
+    assert_num_correct(met["num_correct_tokens"].item(), fwd)
+    assert_loss_close(t2np(met["entropy_sum"]), fwd.entropy_sum, c.dtype, "entropy_sum")
+    assert_grad_close(t2np(gh), rgh, "grad_hidden")
+    assert_grad_close(t2np(gw), rgw, "grad_weight")
+    if B is not None:
+        assert_grad_close(t2np(gb), rgb, "grad_bias")
+    assert flce_lib.get_status(_ws_probe(flce_lib, d)) == 0
+
+
+def _ws_probe(flce, d):
+    """A freshly written forward workspace whose status word reflects `d`'s targets."""
+    import torch
+    n, h = d["hidden"].shape
+    p = flce.make_params(n, h, d["weight"].shape[0], dtype="bf16" if d["hidden"].dtype == torch.bfloat16 else "f32",
+                         reduction="sum")
+    ws = torch.empty(flce.flce_workspace_size(p, flce.FLCE_PASS_FORWARD), dtype=torch.uint8,
+                     device=d["hidden"].device)
+    loss, lse, _ = flce.forward(d["hidden"], d["weight"], d["targets"], d["bias"], reduction="sum",
+                                workspace=ws)
+    return ws
+
+
+def test_all_rows_ignored_mean(flce_lib):
+    import torch
+    c = Case("all_ignored", 300, 64, 500, "bf16", 0.1, reduction="mean", weight_std=0.1)
+    inp = _inputs(c)
+    inp["targets"][:] = si.IGNORE_INDEX
+    d = to_device(inp, c.dtype)
+    loss, lse, met, gh, gw, gb = _run_gpu(flce_lib, c, d)
+    assert torch.isnan(loss).item()
+    assert met["num_correct_tokens"].item() == 0 and met["entropy_sum"].item() == 0.0
+    assert not gh.any().item() and not gw.any().item() and not gb.any().item()
+    X, W, B, T = widened(inp, c.dtype)
+    fwd = oracle.forward(X, W, B, T, reduction="mean")
+    assert_loss_close(t2np(lse), fwd.lse, "bf16", "lse")
+
+
+@pytest.mark.parametrize("reduction", ["sum", "mean", "none"])
+def test_empty_batch(flce_lib, reduction):
+    import torch
+    dev = "cuda"
+    h, v = 64, 300
+    hidden = torch.empty((0, h), dtype=torch.bfloat16, device=dev)
+    weight = torch.randn((v, h), device=dev).to(torch.bfloat16)
+    bias = torch.randn(v, device=dev).to(torch.bfloat16)
+    targets = torch.empty(0, dtype=torch.int64, device=dev)
+    loss, lse, met = flce_lib.forward(hidden, weight, targets, bias, reduction=reduction,
+                                      return_metrics=True)
+    g = torch.ones(1 if reduction != "none" else 0, dtype=torch.float32, device=dev)
+    if reduction == "none":
+        g = torch.ones(1, dtype=torch.float32, device=dev)
+    gh, gw, gb = flce_lib.backward(hidden, weight, targets, lse, g, bias, reduction=reduction)
+    torch.cuda.synchronize()
+    if reduction == "sum":
+        assert loss.item() == 0.0
+    elif reduction == "mean":
+        assert torch.isnan(loss).item()
+    assert met["num_correct_tokens"].item() == 0
+    assert gh.numel() == 0 and not gw.any().item() and not gb.any().item()
+
+
+def test_deterministic_and_metrics_bit_identical(flce_lib):
+    import torch
+    c = Case("determinism", 600, 192, 3000, "bf16", 0.1, 0.8, 8.0, 1e-3, 0.1, "sum", weight_std=0.1)
+    d = to_device(_inputs(c), c.dtype)
+    a = _run_gpu(flce_lib, c, d, return_metrics=True)
+    b = _run_gpu(flce_lib, c, d, return_metrics=False)
+    for x, y, name in ((a[0], b[0], "loss"), (a[1], b[1], "lse"), (a[3], b[3], "grad_hidden"),
+                       (a[4], b[4], "grad_weight"), (a[5], b[5], "grad_bias")):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x, y.view(torch.uint8)
+                           if y.dtype == torch.bfloat16 else y), f"{name} differs between runs"
+    a2 = _run_gpu(flce_lib, c, d, return_metrics=True)
+    assert torch.equal(a[2]["num_correct_tokens"], a2[2]["num_correct_tokens"])
+    assert torch.equal(a[2]["entropy_sum"], a2[2]["entropy_sum"])
+
+
+def test_argmax_ties_take_lowest_index(flce_lib):
+    import torch
+    n, h, v = 256, 64, 600
+    rng = np.random.default_rng(5)
+    x = np.ones((n, h), dtype=np.float32)
+    w = (rng.standard_normal((v, h)) * 0.01).astype(np.float32)
+    w[5] = 0.1
+    w[9] = 0.1          # rows 5 and 9 tie for the maximum on every token
+    w[300] = 0.1        # and so does a row in another 256-wide tile
+    t = np.where(np.arange(n) % 3 == 0, 5, np.where(np.arange(n) % 3 == 1, 9, 300)).astype(np.int64)
+    inp = {"hidden": si.round_to_bf16_bits(x), "weight": si.round_to_bf16_bits(w), "bias": None,
+           "targets": t, "grad_loss": np.array(1.0, dtype=np.float32)}
+    d = to_device(inp, "bf16")
+    _, _, met = flce_lib.forward(d["hidden"], d["weight"], d["targets"], None, reduction="sum",
+                                 return_metrics=True)
+    assert met["num_correct_tokens"].item() == int((t == 5).sum())
+
+
+def test_out_of_range_target_sets_status(flce_lib):
+    import torch
+    c = Case("oob", 300, 64, 500, "bf16", None, reduction="sum", weight_std=0.1)
+    inp = _inputs(c)
+    inp["targets"][7] = 500          # == V: out of range
+    d = to_device(inp, c.dtype)
+    p = flce_lib.make_params(c.n, c.h, c.v, reduction="sum")
+    ws = torch.empty(flce_lib.flce_workspace_size(p, flce_lib.FLCE_PASS_FORWARD), dtype=torch.uint8,
+                     device="cuda")
+    loss, lse, _ = flce_lib.forward(d["hidden"], d["weight"], d["targets"], None, reduction="sum",
+                                    workspace=ws)
+    assert flce_lib.get_status(ws) == flce_lib.FLCE_ERR_TARGET_OUT_OF_RANGE
+    # the row is treated as ignored
+    t = inp["targets"].copy()
+    t[7] = si.IGNORE_INDEX
+    X, W, B, _ = widened(inp, c.dtype)
+    fwd = oracle.forward(X, W, B, t, reduction="sum")
+    assert_loss_close(t2np(loss), fwd.loss, "bf16")
+    wsb = torch.empty(flce_lib.flce_workspace_size(p, flce_lib.FLCE_PASS_BACKWARD), dtype=torch.uint8,
+                      device="cuda")
+    gh, gw, _ = flce_lib.backward(d["hidden"], d["weight"], d["targets"], lse,
+                                  torch.ones(1, device="cuda"), None, reduction="sum", workspace=wsb)
+    assert flce_lib.get_status(wsb) == flce_lib.FLCE_ERR_TARGET_OUT_OF_RANGE
+    assert not gh[7].any().item()
+
+
+def test_host_validation_errors(flce_lib):
+    import torch
+    x = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((100, 64), dtype=torch.bfloat16, device="cuda")
+    t = torch.zeros(16, dtype=torch.int64, device="cuda")
+    with pytest.raises(ValueError):
+        flce_lib.forward(x, w, t, reduction="bogus")
+    p_bad = flce_lib.make_params(16, 64, 100)
+    p_bad.reduction = 7
+    out = torch.empty(16, device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    assert flce_lib.flce_forward(p_bad, x.data_ptr(), w.data_ptr(), None, t.data_ptr(), out.data_ptr(),
+                                 out.data_ptr(), None, None, ws.data_ptr(), ws.numel(),
+                                 None) == flce_lib.FLCE_ERR_INVALID_ARG
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    p = flce_lib.make_params(16, 64, 100)
+    out = torch.empty(1, device="cuda")
+    rc = flce_lib.flce_forward(p, x.data_ptr(), w.data_ptr(), None, t.data_ptr(), out.data_ptr(),
+                               out.data_ptr(), None, None, small_ws.data_ptr(), 16, None)
+    assert rc == flce_lib.FLCE_ERR_WORKSPACE_TOO_SMALL
+
+
+# ----------------------------------------------------------------------------- large workloads
+
+def _sampled_check(flce, wl: si.Workload, n_rows=512, n_vocab=512):
+    import torch
+    c = _from_workload(wl)
+    _say(f"[parity-large] {wl.name}: drawing inputs")
+    inp = si.make_workload_inputs(wl)
+    d = to_device(inp, c.dtype)
+    _say(f"[parity-large] {wl.name}: GPU forward+backward")
+    loss, lse, met, gh, gw, gb = _run_gpu(flce, c, d)
+    loss_n, lse_n = t2np(loss), t2np(lse)
+    nc, ent = met["num_correct_tokens"].item(), met["entropy_sum"].item()
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(c.n, n_rows, replace=False))
+    ign = np.nonzero(inp["targets"] == si.IGNORE_INDEX)[0]
+    if ign.size:
+        rows[:4] = ign[:4]
+        rows = np.unique(rows)
+    valid_t = inp["targets"][inp["targets"] != si.IGNORE_INDEX]
+    vids = np.unique(np.concatenate([rng.choice(c.v, n_vocab // 2, replace=False),
+                                     rng.choice(valid_t, n_vocab // 2)]))
+    gh_s = t2np(gh[torch.from_numpy(rows).cuda()])
+    gw_s = t2np(gw[torch.from_numpy(vids).cuda()])
+    gb_n = t2np(gb)
+    del gh, gw, d
+    torch.cuda.empty_cache()
+    grad_loss = inp["grad_loss"].astype(np.float64)
+    X, W, B, T = widened(inp, c.dtype)
+    del inp["weight"]
+    _say(f"[parity-large] {wl.name}: oracle pass over all rows")
+    fwd, rgb = oracle.full_pass_with_bias_grad(X, W, B, T, grad_loss, **_opts(c))
+    assert_loss_close(loss_n, fwd.loss, c.dtype, "loss")
+    assert_loss_close(lse_n, fwd.lse, c.dtype, "lse")
+    assert_num_correct(nc, fwd)
+    assert_loss_close(ent, fwd.entropy_sum, c.dtype, "entropy_sum")
+    if B is not None:
+        assert_grad_close(gb_n, rgb, "grad_bias")
+    _say(f"[parity-large] {wl.name}: oracle sampled gradients")
+    rgh, rgw = oracle.sampled_gradients(X, W, B, T, grad_loss, fwd.lse, rows, vids, **_opts(c))
+    assert_grad_close(gh_s, rgh, "grad_hidden (sampled rows)")
+    assert_grad_close(gw_s, rgw, "grad_weight (sampled vocab rows)")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["bf16_n8192_h4096_v128256", "bf16_n16384_h2048_v256000",
+                                  "bf16_n8192_h4096_v32000_zipf"])
+def test_full_size_sampled(flce_lib, name):
+    _sampled_check(flce_lib, si.WORKLOADS[name])
