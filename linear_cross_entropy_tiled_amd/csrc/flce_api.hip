@@ -87,6 +87,8 @@ int make_plan(const flce_params* p, Plan* pl) {
   o = align_up(o + size_t(P.N_pad) * 4, 256);
   P.b_D = o;
   o = align_up(o + size_t(P.N_pad) * P.Vc * esize, 256);
+  P.b_xt = o;
+  o = align_up(o + size_t(P.N_pad) * P.H * esize, 256);
   P.b_ghacc = o;
   if (P.dtype == FLCE_BF16 && P.n_chunks > 1) o = align_up(o + size_t(P.N) * P.H * 4, 256);
   P.b_gbpart = o;

@@ -141,7 +141,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dlogits_kernel(DlogitsArgs a) {
   const int v0 = a.cv0 + vt * 256, t0 = tt * 256;
 
   const uint32_t ld = (uint32_t)a.H * E;
-  OperandDesc da, db;
+  OperandDesc da;     // weight rows
+  OperandDesc db;     // hidden rows
   da.base = a.weight + (size_t)v0 * ld;
   da.ld_bytes = ld;
   da.nrec = (uint32_t)max(min(a.V - v0, 256), 0) * ld;
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dlogits_kernel(DlogitsArgs a) {
 // A = hidden (MNMAJOR: rows t, cols h), B = D (MNMAJOR: rows t, cols v).
 // ---------------------------------------------------------------------------
 struct GwArgs {
-  const char* hidden;
+  const char* hiddenT;   // hidden transposed: [H][N_pad], zero past N
   const char* D;
   int ldD;
   int N, H, V, N_pad;
@@ -265,29 +266,29 @@ __global__ __launch_bounds__(256, 1) void bwd_gw_kernel(GwArgs a) {
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
   int ht, vt;
   grouped_tile(L, a.n_ht, a.n_vt_c, 4, ht, vt);
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int h0 = ht * 256, vl0 = vt * 256;
 
-  OperandDesc da, db;
-  const uint32_t ldh = (uint32_t)a.H * E;
-  da.base = a.hidden + (size_t)h0 * E;
-  da.ld_bytes = ldh;
-  da.nrec = a.N > 0 ? (uint32_t)((size_t)a.N * ldh - (size_t)h0 * E) : 0u;
-  da.cols_valid = a.H - h0;
-  da.k_bytes = 0;
+  OperandDesc da;     // hidden^T rows h, K = tokens
+  const uint32_t ldt = (uint32_t)a.N_pad * E;
+  da.base = a.hiddenT + (size_t)h0 * ldt;
+  da.ld_bytes = ldt;
+  da.nrec = (uint32_t)min(a.H - h0, 256) * ldt;
+  da.cols_valid = 0;
+  da.k_bytes = a.N_pad * E;
+  OperandDesc db;     // dlogits rows t (K), columns v: transposing reads
   const uint32_t ldd = (uint32_t)a.ldD * E;
   db.base = a.D + (size_t)vl0 * E;
   db.ld_bytes = ldd;
   db.nrec = a.N_pad > 0 ? (uint32_t)((size_t)a.N_pad * ldd - (size_t)vl0 * E) : 0u;
   db.cols_valid = a.ldD - vl0;
   db.k_bytes = 0;
-  constexpr int kRowsPerStage = kBKB / E;
-  const int KT = (a.N + kRowsPerStage - 1) / kRowsPerStage;
+  const int KT = (a.N_pad * E + kBKB - 1) / kBKB;
 
   f32x16 acc[4][4];
   zero_acc(acc);
-  tile_mainloop<T, false, false>(da, db, KT, acc);
+  tile_mainloop<T, true, false>(da, db, KT, acc);
 
 #pragma unroll
   for (int ni = 0; ni < 4; ni++) {
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(256, 1) void bwd_gh_kernel(GhArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int h0 = ht * 256, t0 = tt * 256;
 
-  OperandDesc da, db;
+  OperandDesc da;     // weight rows v (K) of the chunk, columns h: transposing reads
   const uint32_t ldw = (uint32_t)a.H * E;
   const int vrows = min(a.V - a.cv0, a.cvn);
   da.base = a.weight + ((size_t)a.cv0 * a.H + h0) * E;
@@ -349,6 +350,7 @@ __global__ __launch_bounds__(256, 1) void bwd_gh_kernel(GhArgs a) {
   da.nrec = (uint32_t)((size_t)vrows * ldw - (size_t)h0 * E);
   da.cols_valid = a.H - h0;
   da.k_bytes = 0;
+  OperandDesc db;     // dlogits rows t, K = v
   const uint32_t ldd = (uint32_t)a.ldD * E;
   db.base = a.D + (size_t)t0 * ldd;
   db.ld_bytes = ldd;
@@ -391,6 +393,24 @@ __global__ __launch_bounds__(256, 1) void bwd_gh_kernel(GhArgs a) {
   }
 }
 
+// hidden^T [H][N_pad] (zero for t >= N): the token-contiguous copy of hidden
+// that the grad_weight contraction reads as its register operand.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_hidden_kernel(const T* x, int N, int H, int N_pad, T* xt) {
+  __shared__ float tile[64][65];
+  const int t0 = blockIdx.x * 64, h0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int t = t0 + r, h = h0 + tx;
+    tile[r][tx] = (t < N && h < H) ? load_elem<T>(x, (int64_t)t * H + h) : 0.0f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int h = h0 + r, t = t0 + tx;
+    if (h < H && t < N_pad) xt[(size_t)h * N_pad + t] = (T)tile[tx][r];
+  }
+}
+
 // grad_bias[v] = sum over token tiles of the per-tile column sums, in order.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_gb_reduce(const float* part, int n_tt, int ld, int V, T* gb) {
@@ -430,6 +450,12 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
   pa.status = reinterpret_cast<int*>(ws);
   bwd_prep_kernel<<<1, 1024, 0, st>>>(pa);
 
+  T* hiddenT = reinterpret_cast<T*>(ws + pl.b_xt);
+  if (pl.N > 0) {
+    dim3 grid((unsigned)(pl.N_pad / 64), (unsigned)((pl.H + 63) / 64));
+    transpose_hidden_kernel<T><<<grid, 256, 0, st>>>(reinterpret_cast<const T*>(hidden), (int)pl.N, (int)pl.H,
+                                                     (int)pl.N_pad, hiddenT);
+  }
   const bool gh_f32 = pl.dtype == FLCE_F32;
   float* accb = gh_f32 ? reinterpret_cast<float*>(grad_hidden) : reinterpret_cast<float*>(ws + pl.b_ghacc);
   const int ldD = (int)pl.Vc;
@@ -473,7 +499,7 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
     }
     {
       GwArgs g;
-      g.hidden = static_cast<const char*>(hidden);
+      g.hiddenT = reinterpret_cast<const char*>(hiddenT);
       g.D = D;
       g.ldD = ldD;
       g.N = (int)pl.N;

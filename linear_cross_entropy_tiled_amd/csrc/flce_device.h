@@ -5,14 +5,22 @@
 // Tile main loop: C[256 x 256] += A[256 x K] . B[256 x K]^T with fp32
 // accumulation, 4 waves (2 x 2), each wave owning a 128 x 128 block as 4 x 4
 // tiles of v_mfma_f32_32x32x16_bf16 (v_mfma_f32_32x32x2_f32 for fp32 inputs).
-// Each operand lives in global memory either
-//   KMAJOR  -- rows are the M (or N) index, K contiguous   (weight, hidden as
-//              read by the logit GEMM), or
-//   MNMAJOR -- rows are the K index, M (or N) contiguous   (hidden, weight and
-//              the dlogits scratch as read by the two gradient contractions).
-// Both are staged through LDS as they lie in memory; MNMAJOR fragments are
-// read with ds_read_b64_tr_b16, which transposes 16-bit elements across each
-// group of 16 lanes, so no operand is ever transposed in global memory.
+//
+// Both operands are staged through LDS.  Each lives in global memory either
+//   KMAJOR  -- rows are the M (or N) index, K contiguous   (weight and hidden
+//              as read by the logit GEMM, hidden^T, the dlogits scratch as
+//              read by the grad_hidden contraction), or
+//   MNMAJOR -- rows are the K index, M (or N) contiguous   (the weight and
+//              the dlogits scratch as read by the gradient contractions);
+// MNMAJOR fragments are read with ds_read_b64_tr_b16, which transposes
+// 16-bit elements across each group of 16 lanes.  On gfx950 that read moves
+// about a quarter of the bytes per clock of ds_read_b128, so a contraction
+// uses at most one MNMAJOR operand.
+//
+// K order: a stage is 128 bytes of K per row (64 bf16 / 32 fp32), eight
+// 16-byte chunks.  In sub-step s (0..3) lane half h (lane / 32) contracts
+// chunk 4h + s.  Any order is correct as long as both operands use the same
+// one.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,11 +50,13 @@ constexpr float kMasked = -0x1p100f;
 
 constexpr int kBM = 256;            // tile rows (A operand)
 constexpr int kBN = 256;            // tile cols (B operand)
-constexpr int kBKB = 128;           // bytes of K per pipeline stage per row
+constexpr int kBKB = 128;           // bytes of K per pipeline stage per row (64 bf16 / 32 fp32)
 constexpr int kThreads = 256;       // 4 waves
-constexpr int kOperandStage = kBM * kBKB;           // 32 KiB
-constexpr int kStageBytes = 2 * kOperandStage;      // A + B, 64 KiB
+constexpr int kOperandStage = kBM * kBKB;           // one operand's stage: 32 KiB
+constexpr int kStageBytes = 2 * kOperandStage;      // A + B: 64 KiB
 constexpr int kMainLds = 2 * kStageBytes;           // double buffer, 128 KiB
+constexpr int kBlocksPerWave = kOperandStage / 1024 / 4;   // 1 KiB DMA blocks per wave per operand
+constexpr int kSubsteps = 4;
 constexpr uint32_t kOob = 0x80000000u;              // buffer offset that reads 0
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -92,12 +102,12 @@ __device__ __forceinline__ int acc_row(int mi, int r, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// Operand descriptors and loaders.  Loads go straight from global memory into
-// LDS (buffer_load_dwordx4 ... lds): one wave instruction fills 1 KiB of LDS,
-// lane l writing bytes [16 l, 16 l + 16).  The LDS layouts are swizzled, so
-// each lane fetches the global chunk that belongs at its LDS position.
-// Anything past `nrec` (rows past the end, masked columns, the K tail) reads
-// as zero through the buffer's range check.
+// Operand descriptor and loader.  Loads go straight from global memory
+// into LDS (buffer_load_dwordx4 ... lds): one wave instruction fills 1 KiB of
+// LDS, lane l writing bytes [16 l, 16 l + 16).  The LDS layouts are swizzled,
+// so each lane fetches the global chunk that belongs at its LDS position.
+// Anything past `nrec` (rows past the end, masked columns) reads as zero
+// through the buffer's range check.
 // ---------------------------------------------------------------------------
 struct OperandDesc {
   const char* base;      // KMAJOR: row 0 of the tile; MNMAJOR: element (k=0, col 0 of tile)
@@ -139,8 +149,8 @@ __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
 template <typename T, bool KMAJOR>
 struct OperandLoader {
   i32x4 rsrc;
-  uint32_t voff0, voff1;  // lane offsets (even / odd 1 KiB block for bf16 MNMAJOR)
-  int kc_bytes;           // KMAJOR: this lane's logical chunk column in bytes
+  uint32_t voff0, voff1;  // lane offsets for even / odd 1 KiB blocks
+  int kc_bytes0, kc_bytes1;   // KMAJOR: the lane's logical chunk column (even / odd blocks)
   int k_bytes;
   uint32_t ld_bytes;
   int wave;
@@ -152,14 +162,19 @@ struct OperandLoader {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63;
     if constexpr (KMAJOR) {
-      // block b holds rows 8b..8b+7; lane l -> row 8b + l/8, LDS slot l%8
-      const int row = l >> 3;
-      const int kc = (l & 7) ^ (row & 7);
-      kc_bytes = kc * 16;
-      voff0 = voff1 = (uint32_t)row * d.ld_bytes + kc * 16;
+      // block b holds rows 8b..8b+7 (128 B each); lane l -> row 8b + l/8,
+      // LDS slot l%8, which holds logical chunk slot ^ ((row >> 1) & 7)
+      // = slot ^ ((4b + l/16) & 7): the pattern depends on the parity of b
+      const int row = l >> 3, slot = l & 7;
+      const int kc0 = slot ^ ((l >> 4) & 7);
+      const int kc1 = slot ^ ((4 + (l >> 4)) & 7);
+      kc_bytes0 = kc0 * 16;
+      kc_bytes1 = kc1 * 16;
+      voff0 = (uint32_t)row * d.ld_bytes + kc0 * 16;
+      voff1 = (uint32_t)row * d.ld_bytes + kc1 * 16;
     } else if constexpr (sizeof(T) == 2) {
       // block b holds rows 2b, 2b+1 (512 B each); lane l -> row 2b + l/32, slot l%32
-      kc_bytes = 0;
+      kc_bytes0 = kc_bytes1 = 0;
       const int half = l >> 5, slot = l & 31;
       const int c_even = slot ^ (4 * (half & 3));          // row & 3 = half      (b even)
       const int c_odd = slot ^ (4 * ((2 + half) & 3));     // row & 3 = 2 + half  (b odd)
@@ -167,27 +182,28 @@ struct OperandLoader {
       voff1 = c_odd * 8 < d.cols_valid ? (uint32_t)half * d.ld_bytes + c_odd * 16 : kOob;
     } else {
       // fp32: block b is row b (1 KiB); lane l -> chunk l
-      kc_bytes = 0;
+      kc_bytes0 = kc_bytes1 = 0;
       voff0 = voff1 = l * 4 < d.cols_valid ? (uint32_t)l * 16 : kOob;
     }
   }
 
-  // Issue the 8 direct-to-LDS loads of stage kt (this wave's 8 KiB).
+  // Issue this wave's direct-to-LDS loads of stage kt.
   __device__ __forceinline__ void load(int kt, char* stage) const {
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int b = wave * 8 + i;            // 1 KiB block of the 32 KiB operand stage
+    for (int i = 0; i < kBlocksPerWave; i++) {
+      const int b = wave * kBlocksPerWave + i;   // 1 KiB block of the stage; parity = parity of i
       uint32_t voff, soff;
       if constexpr (KMAJOR) {
         const uint32_t k0 = (uint32_t)kt * kBKB;
-        voff = (int)k0 + kc_bytes < k_bytes ? voff0 : kOob;
+        voff = (i & 1) ? ((int)k0 + kc_bytes1 < k_bytes ? voff1 : kOob)
+                       : ((int)k0 + kc_bytes0 < k_bytes ? voff0 : kOob);
         soff = k0 + (uint32_t)(8 * b) * ld_bytes;
       } else if constexpr (sizeof(T) == 2) {
         voff = (i & 1) ? voff1 : voff0;
-        soff = ((uint32_t)kt * 64 + 2 * b) * ld_bytes;
+        soff = ((uint32_t)kt * (kBKB / 2) + 2 * b) * ld_bytes;
       } else {
         voff = voff0;
-        soff = ((uint32_t)kt * 32 + b) * ld_bytes;
+        soff = ((uint32_t)kt * (kBKB / 4) + b) * ld_bytes;
       }
       dma16(rsrc, __builtin_amdgcn_readfirstlane(lds_addr_of(stage) + b * 1024), voff, soff);
     }
@@ -197,29 +213,35 @@ struct OperandLoader {
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 // ---------------------------------------------------------------------------
-// Fragment reads from LDS.  Sub-step s covers K elements [16s, 16s+16) (bf16)
-// or [8s, 8s+8) (fp32) of the stage.  `c0` is the first tile row/column of the
-// 32-wide MFMA fragment.  Lane l gets row/column c0 + l%32 and K values
-// 16s + 8(l/32) + 0..7 (bf16) -- the same K order for both layouts, so any
-// pairing of a KMAJOR and an MNMAJOR operand contracts consistently.
+// LDS fragment reads.  `c0` is the first tile row/column of the 32-wide MFMA
+// fragment; lane l gets row/column c0 + l%32 and the 16 bytes of K chunk
+// 4(l/32) + s.
 // ---------------------------------------------------------------------------
 template <typename T, bool KMAJOR> struct Frag;
 
+// KMAJOR rows are 128 B; the 16-byte chunk kc of row r sits at slot
+// kc ^ ((r >> 1) & 7).  A ds_read_b128 is served 16 lanes (16 consecutive
+// rows, two per 256-byte bank line) at a time, and this spreads them over all
+// 64 banks.
 template <> struct Frag<bf16, true> {
   typedef bf16x8 type;
   __device__ __forceinline__ static type read(const char* op, int c0, int s, int lane) {
     const int row = c0 + (lane & 31);
-    const int kc = 2 * s + (lane >> 5);
-    const int off = row * kBKB + ((kc ^ (row & 7)) << 4);
+    const int kc = 4 * (lane >> 5) + s;
+    const int off = row * kBKB + ((kc ^ ((row >> 1) & 7)) << 4);
     return *reinterpret_cast<const bf16x8*>(op + off);
   }
 };
 
+// MNMAJOR bf16 rows are 512 B (256 elements); 8-byte unit u of row r sits at
+// unit u ^ ((r & 3) << 3).  The transposing read gives lane i of each 16-lane
+// group element (4 j' + i/4, i%4) of the 16 chunks its group addressed, so the
+// group addresses rows k..k+3 at columns c, c+4, c+8, c+12.
 template <> struct Frag<bf16, false> {
   typedef bf16x8 type;
   __device__ __forceinline__ static type read(const char* op, int c0, int s, int lane) {
     const int g = lane >> 4, kk = lane & 15, j = kk >> 2, q = kk & 3;
-    const int row = 16 * s + 8 * (g >> 1) + j;
+    const int row = 32 * (g >> 1) + 8 * s + j;
     const int u = (c0 >> 2) + 4 * (g & 1) + q;
     const int off = row * 512 + ((u ^ (j << 3)) << 3);
     i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(op + off));
@@ -230,13 +252,13 @@ template <> struct Frag<bf16, false> {
   }
 };
 
-// fp32: lane half h reads K chunk (2s + h), i.e. K = (2s+h)*4 + j for j = 0..3.
+// fp32: chunk kc holds K = 4 kc + j, j = 0..3 (one v_mfma_f32_32x32x2_f32 each).
 template <> struct Frag<float, true> {
   typedef f32x4 type;
   __device__ __forceinline__ static type read(const char* op, int c0, int s, int lane) {
     const int row = c0 + (lane & 31);
-    const int kc = 2 * s + (lane >> 5);
-    const int off = row * kBKB + ((kc ^ (row & 7)) << 4);
+    const int kc = 4 * (lane >> 5) + s;
+    const int off = row * kBKB + ((kc ^ ((row >> 1) & 7)) << 4);
     return *reinterpret_cast<const f32x4*>(op + off);
   }
 };
@@ -245,7 +267,7 @@ template <> struct Frag<float, false> {
   typedef f32x4 type;
   __device__ __forceinline__ static type read(const char* op, int c0, int s, int lane) {
     const int col = c0 + (lane & 31);
-    const int k0 = (2 * s + (lane >> 5)) * 4;
+    const int k0 = (4 * (lane >> 5) + s) * 4;
     f32x4 v;
 #pragma unroll
     for (int j = 0; j < 4; j++) v[j] = *reinterpret_cast<const float*>(op + (k0 + j) * 1024 + col * 4);
@@ -262,36 +284,39 @@ __device__ __forceinline__ void mma(f32x16& c, const f32x4& a, const f32x4& b) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS: two pipeline stages of 64 KiB; kernels also use stage 0 as epilogue
-// scratch after the main loop.
+// LDS: two pipeline stages of 64 KiB (A then B); kernels also use stage 0 as
+// epilogue scratch after the main loop.
 // ---------------------------------------------------------------------------
 static __shared__ __attribute__((aligned(1024))) char g_lds[kMainLds];
 #define g_stage0 (g_lds)
 
+// Fragments of one 16-deep K sub-step: 4 A tiles and 4 B tiles of 32.
 template <typename T, bool A_KMAJOR, bool B_KMAJOR>
-__device__ __forceinline__ void compute_stage(const char* stage, int wm, int wn, int lane,
-                                              f32x16 (&acc)[4][4]) {
-  const char* opA = stage;
-  const char* opB = stage + kOperandStage;
+struct SubstepFrags {
+  typename Frag<T, A_KMAJOR>::type a[4];
+  typename Frag<T, B_KMAJOR>::type b[4];
+
+  __device__ __forceinline__ void read(const char* stage, int s, int wm, int wn, int lane) {
 #pragma unroll
-  for (int s = 0; s < 4; s++) {
-    typename Frag<T, A_KMAJOR>::type fa[4];
-    typename Frag<T, B_KMAJOR>::type fb[4];
+    for (int i = 0; i < 4; i++) a[i] = Frag<T, A_KMAJOR>::read(stage, wm * 128 + i * 32, s, lane);
 #pragma unroll
-    for (int i = 0; i < 4; i++) fa[i] = Frag<T, A_KMAJOR>::read(opA, wm * 128 + i * 32, s, lane);
-#pragma unroll
-    for (int i = 0; i < 4; i++) fb[i] = Frag<T, B_KMAJOR>::read(opB, wn * 128 + i * 32, s, lane);
+    for (int i = 0; i < 4; i++) b[i] = Frag<T, B_KMAJOR>::read(stage + kOperandStage, wn * 128 + i * 32, s, lane);
+  }
+  __device__ __forceinline__ void mma_all(f32x16 (&acc)[4][4]) const {
 #pragma unroll
     for (int mi = 0; mi < 4; mi++)
 #pragma unroll
-      for (int ni = 0; ni < 4; ni++) mma(acc[mi][ni], fa[mi], fb[ni]);
+      for (int ni = 0; ni < 4; ni++) mma(acc[mi][ni], a[mi], b[ni]);
   }
-}
+};
 
 // ---------------------------------------------------------------------------
-// The main loop: stage kt+1 streams into one buffer while stage kt is
-// multiplied out of the other.  acc must be zeroed by the caller.  Ends with
-// a barrier, so the caller may reuse LDS afterwards.
+// The main loop.  Global -> LDS: stage kt+1 streams into one buffer while
+// stage kt is multiplied out of the other.  LDS -> registers: the fragments
+// of sub-step s+1 are read while the 16 MFMAs of sub-step s run, and the
+// first sub-step of the next stage is read right after the stage barrier,
+// under the last 16 MFMAs of the current one.  acc must be zeroed by the
+// caller.  Ends with a barrier, so the caller may reuse LDS afterwards.
 // ---------------------------------------------------------------------------
 template <typename T, bool A_KMAJOR, bool B_KMAJOR>
 __device__ __forceinline__ void tile_mainloop(const OperandDesc& da, const OperandDesc& db, int KT,
@@ -312,16 +337,28 @@ __device__ __forceinline__ void tile_mainloop(const OperandDesc& da, const Opera
   }
   wait_loads();
   __syncthreads();
+  if (KT <= 0) return;
 
+  SubstepFrags<T, A_KMAJOR, B_KMAJOR> f0, f1;
+  f0.read(g_lds, 0, wm, wn, lane);
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) {
-      char* nxt = g_lds + ((kt + 1) & 1) * kStageBytes;
+    const char* cur = g_lds + (kt & 1) * kStageBytes;
+    char* nxt = g_lds + ((kt + 1) & 1) * kStageBytes;
+    const bool more = kt + 1 < KT;
+    if (more) {
       la.load(kt + 1, nxt);
       lb.load(kt + 1, nxt + kOperandStage);
     }
-    compute_stage<T, A_KMAJOR, B_KMAJOR>(g_lds + (kt & 1) * kStageBytes, wm, wn, lane, acc);
+    f1.read(cur, 1, wm, wn, lane);
+    f0.mma_all(acc);
+    f0.read(cur, 2, wm, wn, lane);
+    f1.mma_all(acc);
+    f1.read(cur, 3, wm, wn, lane);
+    f0.mma_all(acc);
     wait_loads();
     __syncthreads();
+    if (more) f0.read(nxt, 0, wm, wn, lane);
+    f1.mma_all(acc);
   }
 }
 

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   }
 
   const uint32_t ld = (uint32_t)a.H * E;
-  OperandDesc db;
+  OperandDesc db;     // hidden rows of this token tile
   db.base = a.hidden + (size_t)t0 * ld;
   db.ld_bytes = ld;
   db.nrec = (uint32_t)min(a.N - t0, 256) * ld;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   f32x16 acc[4][4];
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int v0 = vt * 256;
-    OperandDesc da;
+    OperandDesc da;     // weight rows of this vocabulary tile
     da.base = a.weight + (size_t)v0 * ld;
     da.ld_bytes = ld;
     da.nrec = (uint32_t)min(a.V - v0, 256) * ld;
