@@ -131,13 +131,13 @@ struct DlogitsArgs {
 };
 
 template <typename T, bool HAS_BIAS, bool SOFTCAP>
-__global__ __launch_bounds__(256, 1) void bwd_dlogits_kernel(DlogitsArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a) {
   constexpr int E = sizeof(T);
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
   int vt, tt;
   grouped_tile(L, a.n_vt_c, a.n_tt, 4, vt, tt);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int v0 = a.cv0 + vt * 256, t0 = tt * 256;
 
   const uint32_t ld = (uint32_t)a.H * E;
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dlogits_kernel(DlogitsArgs a) {
   db.k_bytes = a.H * E;
   const int KT = (a.H * E + kBKB - 1) / kBKB;
 
-  f32x16 acc[4][4];
+  f32x16 acc[kMI][kNI];
   zero_acc(acc);
   tile_mainloop<T, true, true>(da, db, KT, acc);
 
@@ -163,23 +163,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dlogits_kernel(DlogitsArgs a) {
   //   D = scale * softcap'(z) * (coefA * p - [row = target] * coefB),
   // stored as 4 consecutive vocabulary rows per lane, plus the column sums
   // over this tile's 256 tokens for grad_bias
-  const int vw = v0 + wm * 128;
-  const bool ragged = vw + 128 > a.V;
-  float cA[4], cB[4], lL[4];
-  int rel[4];
+  const int vw = v0 + wm * kWaveM;
+  const bool ragged = vw + kWaveM > a.V;
+  float cA[kNI], cB[kNI], lL[kNI];
+  int rel[kNI];
 #pragma unroll
-  for (int ni = 0; ni < 4; ni++) {
-    const int t = t0 + wn * 128 + ni * 32 + (lane & 31);
+  for (int ni = 0; ni < kNI; ni++) {
+    const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
     cA[ni] = a.coefA[t];
     cB[ni] = a.coefB[t];
     lL[ni] = a.lseL[t];
     rel[ni] = a.tgt[t] - vw;
   }
   T* D = reinterpret_cast<T*>(a.D);
-  float* xs = reinterpret_cast<float*>(g_stage0);   // [wm][mi][64 lanes]: column sums of the wn = 1 waves
-  float gsum[4];
+  float* xs = reinterpret_cast<float*>(g_stage0);   // [wm][wn][mi][64 lanes]: per-wave column sums
+  float gsum[kMI];
 #pragma unroll
-  for (int mi = 0; mi < 4; mi++) {
+  for (int mi = 0; mi < kMI; mi++) {
     float sb[16];
 #pragma unroll
     for (int g = 0; g < 4; g++) {
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dlogits_kernel(DlogitsArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; r++) cs[r] = 0.0f;
 #pragma unroll
-    for (int ni = 0; ni < 4; ni++) {
+    for (int ni = 0; ni < kNI; ni++) {
       float d[16];
 #pragma unroll
       for (int r = 0; r < 16; r++) {
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dlogits_kernel(DlogitsArgs a) {
         d[r] = v;
         cs[r] += v;
       }
-      const int t = t0 + wn * 128 + ni * 32 + (lane & 31);
+      const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
       T* drow = D + (size_t)t * a.ldD + (vw - a.cv0) + mi * 32 + 4 * (lane >> 5);
 #pragma unroll
       for (int g = 0; g < 4; g++) store4(drow + 8 * g, d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]);
@@ -230,16 +230,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dlogits_kernel(DlogitsArgs a) {
     }
   }
   if constexpr (HAS_BIAS) {
-    if (wn == 1) {
+    // the kWavesN waves with the same wm hold the same vocabulary rows:
+    // add their column sums in wn order
 #pragma unroll
-      for (int mi = 0; mi < 4; mi++) xs[(wm * 4 + mi) * 64 + lane] = gsum[mi];
-    }
+    for (int mi = 0; mi < kMI; mi++) xs[((wm * kWavesN + wn) * kMI + mi) * 64 + lane] = gsum[mi];
     __syncthreads();
     if (wn == 0 && (lane & 1) == 0) {
 #pragma unroll
-      for (int mi = 0; mi < 4; mi++) {
+      for (int mi = 0; mi < kMI; mi++) {
+        float sum = xs[((wm * kWavesN + 0) * kMI + mi) * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < kWavesN; w++) sum += xs[((wm * kWavesN + w) * kMI + mi) * 64 + lane];
         const int row = acc_row(mi, (lane & 31) >> 1, lane);
-        a.gb_part[(size_t)tt * a.ld_gb + vw + row] = gsum[mi] + xs[(wm * 4 + mi) * 64 + lane];
+        a.gb_part[(size_t)tt * a.ld_gb + vw + row] = sum;
       }
     }
   }
@@ -261,13 +264,13 @@ struct GwArgs {
 };
 
 template <typename T>
-__global__ __launch_bounds__(256, 1) void bwd_gw_kernel(GwArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_gw_kernel(GwArgs a) {
   constexpr int E = sizeof(T);
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
   int ht, vt;
   grouped_tile(L, a.n_ht, a.n_vt_c, 4, ht, vt);
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int h0 = ht * 256, vl0 = vt * 256;
 
   OperandDesc da;     // hidden^T rows h, K = tokens
@@ -286,19 +289,19 @@ __global__ __launch_bounds__(256, 1) void bwd_gw_kernel(GwArgs a) {
   db.k_bytes = 0;
   const int KT = (a.N_pad * E + kBKB - 1) / kBKB;
 
-  f32x16 acc[4][4];
+  f32x16 acc[kMI][kNI];
   zero_acc(acc);
   tile_mainloop<T, true, false>(da, db, KT, acc);
 
 #pragma unroll
-  for (int ni = 0; ni < 4; ni++) {
-    const int v = a.cv0 + vl0 + wn * 128 + ni * 32 + (lane & 31);
+  for (int ni = 0; ni < kNI; ni++) {
+    const int v = a.cv0 + vl0 + wn * kWaveN + ni * 32 + (lane & 31);
     if (v >= a.V) continue;
 #pragma unroll
-    for (int mi = 0; mi < 4; mi++)
+    for (int mi = 0; mi < kMI; mi++)
 #pragma unroll
       for (int g = 0; g < 4; g++) {
-        const int h = h0 + wm * 128 + mi * 32 + 8 * g + 4 * (lane >> 5);
+        const int h = h0 + wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5);
         if (h >= a.H) continue;
         const size_t o = (size_t)v * a.H + h;
         if (a.gw_f32)
@@ -333,13 +336,13 @@ struct GhArgs {
 };
 
 template <typename T>
-__global__ __launch_bounds__(256, 1) void bwd_gh_kernel(GhArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_gh_kernel(GhArgs a) {
   constexpr int E = sizeof(T);
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
   int ht, tt;
   grouped_tile(L, a.n_ht, a.n_tt, 4, ht, tt);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int h0 = ht * 256, t0 = tt * 256;
 
   OperandDesc da;     // weight rows v (K) of the chunk, columns h: transposing reads
@@ -359,19 +362,19 @@ __global__ __launch_bounds__(256, 1) void bwd_gh_kernel(GhArgs a) {
   db.k_bytes = a.cvn * E;
   const int KT = (a.cvn * E + kBKB - 1) / kBKB;
 
-  f32x16 acc[4][4];
+  f32x16 acc[kMI][kNI];
   zero_acc(acc);
   tile_mainloop<T, false, true>(da, db, KT, acc);
 
 #pragma unroll
-  for (int ni = 0; ni < 4; ni++) {
-    const int t = t0 + wn * 128 + ni * 32 + (lane & 31);
+  for (int ni = 0; ni < kNI; ni++) {
+    const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
     if (t >= a.N) continue;
 #pragma unroll
-    for (int mi = 0; mi < 4; mi++)
+    for (int mi = 0; mi < kMI; mi++)
 #pragma unroll
       for (int g = 0; g < 4; g++) {
-        const int h = h0 + wm * 128 + mi * 32 + 8 * g + 4 * (lane >> 5);
+        const int h = h0 + wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5);
         if (h >= a.H) continue;
         const size_t o = (size_t)t * a.H + h;
         float c0 = acc[mi][ni][4 * g], c1 = acc[mi][ni][4 * g + 1];
@@ -490,11 +493,11 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       d.ld_gb = (int)pl.V_pad;
       const int nwg = n_vt_c * (int)pl.n_tt;
       if (pl.has_bias) {
-        if (pl.cap > 0) bwd_dlogits_kernel<T, true, true><<<nwg, 256, 0, st>>>(d);
-        else bwd_dlogits_kernel<T, true, false><<<nwg, 256, 0, st>>>(d);
+        if (pl.cap > 0) bwd_dlogits_kernel<T, true, true><<<nwg, kThreads, 0, st>>>(d);
+        else bwd_dlogits_kernel<T, true, false><<<nwg, kThreads, 0, st>>>(d);
       } else {
-        if (pl.cap > 0) bwd_dlogits_kernel<T, false, true><<<nwg, 256, 0, st>>>(d);
-        else bwd_dlogits_kernel<T, false, false><<<nwg, 256, 0, st>>>(d);
+        if (pl.cap > 0) bwd_dlogits_kernel<T, false, true><<<nwg, kThreads, 0, st>>>(d);
+        else bwd_dlogits_kernel<T, false, false><<<nwg, kThreads, 0, st>>>(d);
       }
     }
     {
@@ -511,7 +514,7 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       g.n_vt_c = n_vt_c;
       g.gw = grad_weight;
       g.gw_f32 = pl.gw_dtype == FLCE_F32;
-      bwd_gw_kernel<T><<<(int)pl.n_ht * n_vt_c, 256, 0, st>>>(g);
+      bwd_gw_kernel<T><<<(int)pl.n_ht * n_vt_c, kThreads, 0, st>>>(g);
     }
     if (pl.N > 0) {
       GhArgs h;
@@ -529,7 +532,7 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       h.out = grad_hidden;
       h.out_f32 = gh_f32;
       h.mode = pl.n_chunks == 1 ? 3 : (c == 0 ? 0 : (c == pl.n_chunks - 1 ? 2 : 1));
-      bwd_gh_kernel<T><<<(int)(pl.n_ht * pl.n_tt), 256, 0, st>>>(h);
+      bwd_gh_kernel<T><<<(int)(pl.n_ht * pl.n_tt), kThreads, 0, st>>>(h);
     }
   }
   if (grad_bias) {

@@ -3,8 +3,11 @@
 // shared 256x256 MFMA tile main loop.
 //
 // Tile main loop: C[256 x 256] += A[256 x K] . B[256 x K]^T with fp32
-// accumulation, 4 waves (2 x 2), each wave owning a 128 x 128 block as 4 x 4
-// tiles of v_mfma_f32_32x32x16_bf16 (v_mfma_f32_32x32x2_f32 for fp32 inputs).
+// accumulation, 8 waves (2 along M x 4 along N, two per SIMD), each wave
+// owning a 128 x 64 block as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16
+// (v_mfma_f32_32x32x2_f32 for fp32 inputs).  Two waves per SIMD keep enough
+// LDS reads in flight to feed the matrix cores; with one wave per SIMD
+// (4 x 128 x 128) the same loop runs about 15% slower.
 //
 // Both operands are staged through LDS.  Each lives in global memory either
 //   KMAJOR  -- rows are the M (or N) index, K contiguous   (weight and hidden
@@ -51,11 +54,15 @@ constexpr float kMasked = -0x1p100f;
 constexpr int kBM = 256;            // tile rows (A operand)
 constexpr int kBN = 256;            // tile cols (B operand)
 constexpr int kBKB = 128;           // bytes of K per pipeline stage per row (64 bf16 / 32 fp32)
-constexpr int kThreads = 256;       // 4 waves
+constexpr int kWavesM = 2, kWavesN = 4;
+constexpr int kWaves = kWavesM * kWavesN;        // 8 waves
+constexpr int kThreads = 64 * kWaves;            // 512 threads
+constexpr int kMI = 4, kNI = 2;                  // 32 x 32 MFMA tiles per wave (M x N)
+constexpr int kWaveM = 32 * kMI, kWaveN = 32 * kNI;   // 128 x 64
 constexpr int kOperandStage = kBM * kBKB;           // one operand's stage: 32 KiB
 constexpr int kStageBytes = 2 * kOperandStage;      // A + B: 64 KiB
 constexpr int kMainLds = 2 * kStageBytes;           // double buffer, 128 KiB
-constexpr int kBlocksPerWave = kOperandStage / 1024 / 4;   // 1 KiB DMA blocks per wave per operand
+constexpr int kBlocksPerWave = kOperandStage / 1024 / kWaves;   // 1 KiB DMA blocks per wave per operand
 constexpr int kSubsteps = 4;
 constexpr uint32_t kOob = 0x80000000u;              // buffer offset that reads 0
 
@@ -290,23 +297,24 @@ __device__ __forceinline__ void mma(f32x16& c, const f32x4& a, const f32x4& b) {
 static __shared__ __attribute__((aligned(1024))) char g_lds[kMainLds];
 #define g_stage0 (g_lds)
 
-// Fragments of one 16-deep K sub-step: 4 A tiles and 4 B tiles of 32.
+// Fragments of one 16-deep K sub-step: kMI A tiles and kNI B tiles of 32.
 template <typename T, bool A_KMAJOR, bool B_KMAJOR>
 struct SubstepFrags {
-  typename Frag<T, A_KMAJOR>::type a[4];
-  typename Frag<T, B_KMAJOR>::type b[4];
+  typename Frag<T, A_KMAJOR>::type a[kMI];
+  typename Frag<T, B_KMAJOR>::type b[kNI];
 
   __device__ __forceinline__ void read(const char* stage, int s, int wm, int wn, int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) a[i] = Frag<T, A_KMAJOR>::read(stage, wm * 128 + i * 32, s, lane);
+    for (int i = 0; i < kMI; i++) a[i] = Frag<T, A_KMAJOR>::read(stage, wm * kWaveM + i * 32, s, lane);
 #pragma unroll
-    for (int i = 0; i < 4; i++) b[i] = Frag<T, B_KMAJOR>::read(stage + kOperandStage, wn * 128 + i * 32, s, lane);
+    for (int i = 0; i < kNI; i++)
+      b[i] = Frag<T, B_KMAJOR>::read(stage + kOperandStage, wn * kWaveN + i * 32, s, lane);
   }
-  __device__ __forceinline__ void mma_all(f32x16 (&acc)[4][4]) const {
+  __device__ __forceinline__ void mma_all(f32x16 (&acc)[kMI][kNI]) const {
 #pragma unroll
-    for (int mi = 0; mi < 4; mi++)
+    for (int mi = 0; mi < kMI; mi++)
 #pragma unroll
-      for (int ni = 0; ni < 4; ni++) mma(acc[mi][ni], a[mi], b[ni]);
+      for (int ni = 0; ni < kNI; ni++) mma(acc[mi][ni], a[mi], b[ni]);
   }
 };
 
@@ -320,11 +328,11 @@ struct SubstepFrags {
 // ---------------------------------------------------------------------------
 template <typename T, bool A_KMAJOR, bool B_KMAJOR>
 __device__ __forceinline__ void tile_mainloop(const OperandDesc& da, const OperandDesc& db, int KT,
-                                              f32x16 (&acc)[4][4]) {
+                                              f32x16 (&acc)[kMI][kNI]) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
 
   OperandLoader<T, A_KMAJOR> la;
   OperandLoader<T, B_KMAJOR> lb;
@@ -362,11 +370,11 @@ __device__ __forceinline__ void tile_mainloop(const OperandDesc& da, const Opera
   }
 }
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[kMI][kNI]) {
 #pragma unroll
-  for (int mi = 0; mi < 4; mi++)
+  for (int mi = 0; mi < kMI; mi++)
 #pragma unroll
-    for (int ni = 0; ni < 4; ni++)
+    for (int ni = 0; ni < kNI; ni++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[mi][ni][r] = 0.0f;
 }

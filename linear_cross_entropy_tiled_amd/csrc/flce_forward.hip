@@ -63,21 +63,21 @@ __device__ __forceinline__ void load_bias4(const T* b, int r0, int V, float* out
 }
 
 template <typename T, bool HAS_BIAS, bool SOFTCAP>
-__global__ __launch_bounds__(256, 1) void fwd_tiles_kernel(FwdTileArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   constexpr int E = sizeof(T);
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
   const int tt = L / a.S, s = L % a.S;
   const int vt_begin = (int)((int64_t)s * a.n_vt / a.S);
   const int vt_end = (int)((int64_t)(s + 1) * a.n_vt / a.S);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int t0 = tt * 256;
 
-  int tgt[4];
-  RowState st[4];
+  int tgt[kNI];
+  RowState st[kNI];
 #pragma unroll
-  for (int ni = 0; ni < 4; ni++) {
-    const int t = t0 + wn * 128 + ni * 32 + (lane & 31);
+  for (int ni = 0; ni < kNI; ni++) {
+    const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
     const int64_t tv = t < a.N ? a.targets[t] : a.ignore_index;
     tgt[ni] = (tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1;
     st[ni].m = kMasked;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   db.k_bytes = a.H * E;
   const int KT = (a.H * E + kBKB - 1) / kBKB;
 
-  f32x16 acc[4][4];
+  f32x16 acc[kMI][kNI];
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int v0 = vt * 256;
     OperandDesc da;     // weight rows of this vocabulary tile
@@ -111,10 +111,10 @@ __global__ __launch_bounds__(256, 1) void fwd_tiles_kernel(FwdTileArgs a) {
     // ---- epilogue: transform each 32-row MFMA tile and merge it into the
     // running state of its token column (rows visited in ascending order, so
     // a strict > keeps the lowest index on ties)
-    const int vw = v0 + wm * 128;
-    const bool ragged = vw + 128 > a.V;
+    const int vw = v0 + wm * kWaveM;
+    const bool ragged = vw + kWaveM > a.V;
 #pragma unroll
-    for (int mi = 0; mi < 4; mi++) {
+    for (int mi = 0; mi < kMI; mi++) {
       float sb[16];
 #pragma unroll
       for (int g = 0; g < 4; g++) {
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256, 1) void fwd_tiles_kernel(FwdTileArgs a) {
         for (int j = 0; j < 4; j++) sb[4 * g + j] = a.scale * b4[j];
       }
 #pragma unroll
-      for (int ni = 0; ni < 4; ni++) {
+      for (int ni = 0; ni < kNI; ni++) {
         float z[16];
         float mx = kMasked;
         int ix = 0;
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256, 1) void fwd_tiles_kernel(FwdTileArgs a) {
 
   // ---- merge the two lane halves (same tokens, interleaved rows)
 #pragma unroll
-  for (int ni = 0; ni < 4; ni++) {
+  for (int ni = 0; ni < kNI; ni++) {
     RowState o;
     o.m = __shfl_xor(st[ni].m, 32);
     o.l = __shfl_xor(st[ni].l, 32);
@@ -183,33 +183,34 @@ __global__ __launch_bounds__(256, 1) void fwd_tiles_kernel(FwdTileArgs a) {
     merge_state(st[ni], o);
   }
   // ---- merge the two M waves through LDS, then write the split's partials
-  float* xs = reinterpret_cast<float*>(g_stage0);   // [wn][field][128]
+  static_assert(kWavesM == 2, "the merge below pairs two waves along M");
+  float* xs = reinterpret_cast<float*>(g_stage0);   // [wn][field][kWaveN]
   if (wm == 1 && lane < 32) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ni++) {
+    for (int ni = 0; ni < kNI; ni++) {
       const int c = ni * 32 + lane;
-      float* p = xs + wn * 5 * 128;
-      p[0 * 128 + c] = st[ni].m;
-      p[1 * 128 + c] = st[ni].l;
-      p[2 * 128 + c] = st[ni].T;
-      p[3 * 128 + c] = st[ni].zt;
-      p[4 * 128 + c] = __int_as_float(st[ni].idx);
+      float* p = xs + wn * 5 * kWaveN;
+      p[0 * kWaveN + c] = st[ni].m;
+      p[1 * kWaveN + c] = st[ni].l;
+      p[2 * kWaveN + c] = st[ni].T;
+      p[3 * kWaveN + c] = st[ni].zt;
+      p[4 * kWaveN + c] = __int_as_float(st[ni].idx);
     }
   }
   __syncthreads();
   if (wm == 0 && lane < 32) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ni++) {
+    for (int ni = 0; ni < kNI; ni++) {
       const int c = ni * 32 + lane;
-      const float* p = xs + wn * 5 * 128;
+      const float* p = xs + wn * 5 * kWaveN;
       RowState o;
-      o.m = p[0 * 128 + c];
-      o.l = p[1 * 128 + c];
-      o.T = p[2 * 128 + c];
-      o.zt = p[3 * 128 + c];
-      o.idx = __float_as_int(p[4 * 128 + c]);
+      o.m = p[0 * kWaveN + c];
+      o.l = p[1 * kWaveN + c];
+      o.T = p[2 * kWaveN + c];
+      o.zt = p[3 * kWaveN + c];
+      o.idx = __float_as_int(p[4 * kWaveN + c]);
       merge_state(st[ni], o);
-      const int t = t0 + wn * 128 + c;
+      const int t = t0 + wn * kWaveN + c;
       const size_t o_ = (size_t)s * a.N_pad + t;
       a.part_m[o_] = st[ni].m;
       a.part_l[o_] = st[ni].l;
@@ -358,11 +359,11 @@ __global__ __launch_bounds__(256) void fwd_finalize_scalars(ScalarArgs a) {
 template <typename T>
 static void launch_fwd_tiles(const Plan& pl, const FwdTileArgs& args, int nwg, hipStream_t st) {
   if (pl.has_bias) {
-    if (pl.cap > 0) fwd_tiles_kernel<T, true, true><<<nwg, 256, 0, st>>>(args);
-    else fwd_tiles_kernel<T, true, false><<<nwg, 256, 0, st>>>(args);
+    if (pl.cap > 0) fwd_tiles_kernel<T, true, true><<<nwg, kThreads, 0, st>>>(args);
+    else fwd_tiles_kernel<T, true, false><<<nwg, kThreads, 0, st>>>(args);
   } else {
-    if (pl.cap > 0) fwd_tiles_kernel<T, false, true><<<nwg, 256, 0, st>>>(args);
-    else fwd_tiles_kernel<T, false, false><<<nwg, 256, 0, st>>>(args);
+    if (pl.cap > 0) fwd_tiles_kernel<T, false, true><<<nwg, kThreads, 0, st>>>(args);
+    else fwd_tiles_kernel<T, false, false><<<nwg, kThreads, 0, st>>>(args);
   }
 }
 
