@@ -17,6 +17,8 @@ fp64 CPU oracle on a bounded slice of the same workload.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +35,37 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "fwd+bwd tokens/s and TFLOP/s (8NHV) vs bf16 MFMA peak, N=8192 H=4096 V=128k"
+CSRC = os.path.join(ROOT, "linear_cross_entropy_tiled_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; a traffic figure is only reported for the
+    kernels it was measured on."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(CSRC, "*.hip"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the forward tile kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None if it is stale."""
+    path = os.path.join(PROFILES, f"traffic_fwd_tiles_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _to_dev(inp, dtype):
@@ -78,7 +111,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, copy this many MiB device-to-device once (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -123,6 +158,13 @@ def main():
         if rc:
             raise flce.FlceError(rc, "flce_backward")
 
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         fwd()
         bwd()
@@ -175,7 +217,8 @@ def main():
         # finalize kernels; its HIP-event time bounds the tile kernel's time
         "roofline": {"bound": "mfma", "kernel": "fwd_tiles_kernel (+ finalize)",
                      "achieved": fwd_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": fwd_tflops / peak, "traffic": None},
+                     "frac": fwd_tflops / peak, "traffic": measured_traffic(wl.name)},
+        "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
         del d
