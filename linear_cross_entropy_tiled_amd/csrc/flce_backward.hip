@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
 
   f32x16 acc[kMI][kNI];
   zero_acc(acc);
-  tile_mainloop<T, true, true>(da, db, KT, acc);
+  tile_mainloop<T, true, true>(da, db, KT, grouped_share(vt, tt), acc);
 
   // ---- epilogue, one 32-row MFMA tile at a time:
   //   D = scale * softcap'(z) * (coefA * p - [row = target] * coefB),
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gw_kernel(GwArgs a) {
 
   f32x16 acc[kMI][kNI];
   zero_acc(acc);
-  tile_mainloop<T, true, false>(da, db, KT, acc);
+  tile_mainloop<T, true, false>(da, db, KT, grouped_share(ht, vt), acc);
 
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gh_kernel(GhArgs a) {
 
   f32x16 acc[kMI][kNI];
   zero_acc(acc);
-  tile_mainloop<T, false, true>(da, db, KT, acc);
+  tile_mainloop<T, false, true>(da, db, KT, grouped_share(ht, tt), acc);
 
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {

@@ -149,6 +149,16 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_addr, uint
                : "memory");
 }
 
+// 4-byte direct-to-LDS load used only to pull a line into L2: every lane's
+// word lands in a small sink that is never read.  Offsets >= the descriptor's
+// range (kOob) fetch nothing.
+__device__ __forceinline__ void dma4_sink(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((const LDS_AS char*)p);
 }
@@ -194,6 +204,16 @@ struct OperandLoader {
     }
   }
 
+  // L2 prefetch of 128-byte line j (0..255) of stage kt: K-major row j;
+  // M/N-major bf16 row 64 kt + j/4, column block j%4.  Inactive lanes fetch
+  // nothing.
+  __device__ __forceinline__ void prefetch_line(int kt, int j, bool active, uint32_t sink) const {
+    uint32_t voff;
+    if constexpr (KMAJOR) voff = (uint32_t)j * ld_bytes + (uint32_t)kt * kBKB;
+    else voff = (uint32_t)(kt * (kBKB / 2) + (j >> 2)) * ld_bytes + (uint32_t)(j & 3) * 128;
+    dma4_sink(rsrc, sink, active ? voff : kOob);
+  }
+
   // Issue this wave's direct-to-LDS loads of stage kt.
   __device__ __forceinline__ void load(int kt, char* stage) const {
 #pragma unroll
@@ -218,6 +238,9 @@ struct OperandLoader {
 };
 
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// vmcnt(1): all but the most recent vector-memory load have completed (loads
+// complete in issue order)
+__device__ __forceinline__ void wait_vmcnt_1() { __builtin_amdgcn_s_waitcnt(0x0F71); }
 
 // ---------------------------------------------------------------------------
 // LDS fragment reads.  `c0` is the first tile row/column of the 32-wide MFMA
@@ -318,17 +341,94 @@ struct SubstepFrags {
   }
 };
 
+// Shared-tile L2 prefetch.  The 32 workgroups that one XCD runs at once
+// cover a few A tiles and a few B tiles, each read by several of them in step.
+// Workgroup `a_rank` of the `a_n` that read the same A tile fetches its
+// 1/a_n of the tile's lines two stages ahead (likewise for B), so that the
+// others' loads hit in L2 instead of all waiting on the same misses.
+// a_n = 0 (or b_n = 0) turns it off for that operand.
+struct L2Share {
+  int a_rank, a_n, b_rank, b_n;
+};
+constexpr int kPrefetchAhead = 2;
+static __shared__ __attribute__((aligned(256))) char g_prefetch_sink[256];
+
+// Issues this wave's share of the prefetch of stage kt (bf16 only); returns
+// whether the wave issued a load (wave-uniform).
+template <typename T, bool A_KMAJOR, bool B_KMAJOR>
+__device__ __forceinline__ bool prefetch_stage(const OperandLoader<T, A_KMAJOR>& la,
+                                               const OperandLoader<T, B_KMAJOR>& lb, const L2Share& sh,
+                                               int kt, int wave, int lane) {
+  if constexpr (sizeof(T) != 2) {
+    return false;
+  } else {
+    // waves 0-3 take A's lines, 64 each; waves 4-7 take B's
+    const bool is_a = wave < 4;
+    const int n = is_a ? sh.a_n : sh.b_n;
+    if (n <= 0) return false;
+    const int rank = is_a ? sh.a_rank : sh.b_rank;
+    const int first = rank * 256 / n, count = (rank + 1) * 256 / n - first;
+    const int off = (wave & 3) * 64;
+    if (off >= count) return false;
+    const uint32_t sink = __builtin_amdgcn_readfirstlane(lds_addr_of(g_prefetch_sink));
+    const bool active = off + lane < count;
+    if (is_a) la.prefetch_line(kt, first + off + lane, active, sink);
+    else lb.prefetch_line(kt, first + off + lane, active, sink);
+    return true;
+  }
+}
+
+// Instruction order inside one sub-step (bf16): the kMI x kNI = 8 MFMAs with
+// the NR LDS reads of the next sub-step slotted between them, front-loaded so
+// the reads are back before they are needed.  Left to itself the compiler
+// clusters the reads right before their first use and then waits on them.
+template <int NR, int I = 0>
+__device__ __forceinline__ void interleave_mfma_reads() {
+  static_assert(kMI * kNI == 8, "the pattern assumes 8 MFMAs per sub-step");
+  if constexpr (I < 8) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    constexpr int per = (NR + 5) / 6;
+    constexpr int lo = I * per < NR ? I * per : NR;
+    constexpr int hi = (I + 1) * per < NR ? (I + 1) * per : NR;
+    if constexpr (hi > lo) __builtin_amdgcn_sched_group_barrier(0x100, hi - lo, 0);   // LDS reads
+    interleave_mfma_reads<NR, I + 1>();
+  }
+}
+
+// LDS read instructions per sub-step: one per K-major fragment, two
+// (transposing 8-byte reads) per M/N-major bf16 fragment.
+template <bool A_KMAJOR, bool B_KMAJOR>
+constexpr int reads_per_substep() {
+  return (A_KMAJOR ? kMI : 2 * kMI) + (B_KMAJOR ? kNI : 2 * kNI);
+}
+
+// One sub-step: MFMAs on `cur` while `nxt` is read from `stage`, sub-step s.
+template <typename T, bool A_KMAJOR, bool B_KMAJOR>
+__device__ __forceinline__ void substep(const SubstepFrags<T, A_KMAJOR, B_KMAJOR>& cur,
+                                        SubstepFrags<T, A_KMAJOR, B_KMAJOR>& nxt, const char* stage, int s,
+                                        int wm, int wn, int lane, f32x16 (&acc)[kMI][kNI]) {
+  if constexpr (sizeof(T) == 2) __builtin_amdgcn_sched_barrier(0);
+  nxt.read(stage, s, wm, wn, lane);
+  cur.mma_all(acc);
+  if constexpr (sizeof(T) == 2) {
+    interleave_mfma_reads<reads_per_substep<A_KMAJOR, B_KMAJOR>()>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The main loop.  Global -> LDS: stage kt+1 streams into one buffer while
 // stage kt is multiplied out of the other.  LDS -> registers: the fragments
-// of sub-step s+1 are read while the 16 MFMAs of sub-step s run, and the
+// of sub-step s+1 are read while the 8 MFMAs of sub-step s run, and the
 // first sub-step of the next stage is read right after the stage barrier,
-// under the last 16 MFMAs of the current one.  acc must be zeroed by the
-// caller.  Ends with a barrier, so the caller may reuse LDS afterwards.
+// under the last MFMAs of the current one.  acc must be zeroed by the
+// caller.  Every LDS read whose value is used completes before the last
+// barrier (the reads after it fill fragments that are discarded), so the
+// caller may write LDS as soon as the loop returns.
 // ---------------------------------------------------------------------------
 template <typename T, bool A_KMAJOR, bool B_KMAJOR>
 __device__ __forceinline__ void tile_mainloop(const OperandDesc& da, const OperandDesc& db, int KT,
-                                              f32x16 (&acc)[kMI][kNI]) {
+                                              const L2Share& sh, f32x16 (&acc)[kMI][kNI]) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
@@ -352,21 +452,21 @@ __device__ __forceinline__ void tile_mainloop(const OperandDesc& da, const Opera
   for (int kt = 0; kt < KT; ++kt) {
     const char* cur = g_lds + (kt & 1) * kStageBytes;
     char* nxt = g_lds + ((kt + 1) & 1) * kStageBytes;
-    const bool more = kt + 1 < KT;
-    if (more) {
+    if (kt + 1 < KT) {
       la.load(kt + 1, nxt);
       lb.load(kt + 1, nxt + kOperandStage);
     }
-    f1.read(cur, 1, wm, wn, lane);
-    f0.mma_all(acc);
-    f0.read(cur, 2, wm, wn, lane);
-    f1.mma_all(acc);
-    f1.read(cur, 3, wm, wn, lane);
-    f0.mma_all(acc);
-    wait_loads();
+    const bool pf = kt + kPrefetchAhead < KT &&
+                    prefetch_stage<T, A_KMAJOR, B_KMAJOR>(la, lb, sh, kt + kPrefetchAhead, wave, lane);
+    substep(f0, f1, cur, 1, wm, wn, lane, acc);
+    substep(f1, f0, cur, 2, wm, wn, lane, acc);
+    substep(f0, f1, cur, 3, wm, wn, lane, acc);
+    // stage kt+1 must be in LDS; the prefetch issued after it may still be in flight
+    if (pf) wait_vmcnt_1();
+    else wait_loads();
     __syncthreads();
-    if (more) f0.read(nxt, 0, wm, wn, lane);
-    f1.mma_all(acc);
+    // after the last stage this reads stale (in-bounds) LDS that is never used
+    substep(f1, f0, nxt, 0, wm, wn, lane, acc);
   }
 }
 
@@ -396,6 +496,18 @@ __device__ __forceinline__ void grouped_tile(int id, int n_m, int n_n, int gm, i
   const int in = id - group * per_group;
   tm = first + in % size;
   tn = in / size;
+}
+
+// Prefetch shares under grouped_tile(..., 4, ...) when one XCD runs 32
+// consecutive ids at a time: 4 M-tiles x 8 N-tiles, so each A tile is read by
+// the 8 workgroups of distinct tn and each B tile by the 4 of distinct tm.
+__device__ __forceinline__ L2Share grouped_share(int tm, int tn) {
+  L2Share s;
+  s.a_rank = tn & 7;
+  s.a_n = 8;
+  s.b_rank = tm & 3;
+  s.b_n = 4;
+  return s;
 }
 
 template <typename T> __device__ __forceinline__ float load_elem(const T* p, int64_t i);

@@ -96,6 +96,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   db.k_bytes = a.H * E;
   const int KT = (a.H * E + kBKB - 1) / kBKB;
 
+  // One XCD runs `win` consecutive ids at once: win/S token tiles x S splits.
+  // The S splits of a token tile share its hidden rows; the win/S token tiles
+  // of a split read the same weight tile at the same time.
+  const int win = min(32, max(1, (int)gridDim.x / 8));
+  L2Share sh;
+  sh.b_n = min(a.S, win);
+  sh.b_rank = s % sh.b_n;
+  sh.a_n = a.S <= win ? win / a.S : 1;
+  sh.a_rank = tt % sh.a_n;
+  if (sh.a_n < 2) sh.a_n = 0;
+  if (sh.b_n < 2) sh.b_n = 0;
+
   f32x16 acc[kMI][kNI];
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int v0 = vt * 256;
@@ -106,7 +118,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
     da.cols_valid = 0;
     da.k_bytes = a.H * E;
     zero_acc(acc);
-    tile_mainloop<T, true, true>(da, db, KT, acc);
+    tile_mainloop<T, true, true>(da, db, KT, sh, acc);
 
     // ---- epilogue: transform each 32-row MFMA tile and merge it into the
     // running state of its token column (rows visited in ascending order, so
