@@ -163,6 +163,35 @@ __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((const LDS_AS char*)p);
 }
 
+// One wave copies `nbytes` (a multiple of 256) from global `src` to LDS `dst`
+// by direct-to-LDS loads, 4 bytes per lane per 256-byte block; bytes at or
+// past `valid_bytes` arrive as 0.  The caller waits for vmcnt and
+// synchronises before reading (the main loop's first stage wait does both).
+__device__ __forceinline__ void dma_vector(const void* src, uint32_t valid_bytes, char* dst, int nbytes,
+                                           int lane) {
+  const i32x4 r = make_rsrc_words(src, valid_bytes);
+  const uint32_t base = lds_addr_of(dst);
+  for (int b = 0; b < nbytes; b += 256) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(base + b)), "v"((uint32_t)(b + 4 * lane)), "s"(r)
+                 : "memory");
+  }
+}
+
+// Four consecutive entries of a vector staged in LDS, widened to fp32.
+template <typename T> __device__ __forceinline__ void lds_vec4(const char* v, int i, float* out);
+template <> __device__ __forceinline__ void lds_vec4<float>(const char* v, int i, float* out) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(v + 4 * i);
+#pragma unroll
+  for (int j = 0; j < 4; j++) out[j] = x[j];
+}
+template <> __device__ __forceinline__ void lds_vec4<bf16>(const char* v, int i, float* out) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(v + 2 * i);
+#pragma unroll
+  for (int j = 0; j < 4; j++) out[j] = (float)x[j];
+}
+
 template <typename T, bool KMAJOR>
 struct OperandLoader {
   i32x4 rsrc;

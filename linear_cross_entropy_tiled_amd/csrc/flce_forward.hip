@@ -43,25 +43,6 @@ __device__ __forceinline__ void merge_state(RowState& a, const RowState& b) {
   a.zt = fmaxf(a.zt, b.zt);
 }
 
-// Loads 4 consecutive bias entries starting at row `r0`, zero past V.
-template <typename T>
-__device__ __forceinline__ void load_bias4(const T* b, int r0, int V, float* out) {
-  if (r0 + 3 < V) {
-    if constexpr (sizeof(T) == 2) {
-      const bf16x4 v = *reinterpret_cast<const bf16x4*>(b + r0);
-#pragma unroll
-      for (int j = 0; j < 4; j++) out[j] = (float)v[j];
-    } else {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(b + r0);
-#pragma unroll
-      for (int j = 0; j < 4; j++) out[j] = v[j];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; j++) out[j] = (r0 + j < V) ? load_elem<T>(b, r0 + j) : 0.0f;
-  }
-}
-
 template <typename T, bool HAS_BIAS, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   constexpr int E = sizeof(T);
@@ -108,9 +89,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   if (sh.a_n < 2) sh.a_n = 0;
   if (sh.b_n < 2) sh.b_n = 0;
 
+  // the bias of each vocabulary tile is staged in LDS (two buffers, by tile
+  // parity: a tile's bias is written only after every wave has passed the
+  // barriers of the tile in between, i.e. finished reading the older one)
+  static __shared__ __attribute__((aligned(16))) char bias_lds[2][256 * sizeof(T)];
+
   f32x16 acc[kMI][kNI];
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int v0 = vt * 256;
+    const char* bias_tile = bias_lds[(vt - vt_begin) & 1];
+    // the range is rounded up to whole 4-byte words so that an odd last bf16
+    // entry still arrives: its word lies in the same page as the entry (the
+    // bias is 16-byte aligned), and its other half only feeds masked rows
+    if (HAS_BIAS && wave == 0)
+      dma_vector(reinterpret_cast<const T*>(a.bias) + v0, ((uint32_t)min(a.V - v0, 256) * E + 3u) & ~3u,
+                 bias_lds[(vt - vt_begin) & 1], 256 * E, lane);
     OperandDesc da;     // weight rows of this vocabulary tile
     da.base = a.weight + (size_t)v0 * ld;
     da.ld_bytes = ld;
@@ -121,38 +114,40 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
     tile_mainloop<T, true, true>(da, db, KT, sh, acc);
 
     // ---- epilogue: transform each 32-row MFMA tile and merge it into the
-    // running state of its token column (rows visited in ascending order, so
-    // a strict > keeps the lowest index on ties)
+    // running state of its token column.  Rows are visited in ascending
+    // order, so taking an index only on a strict improvement of the running
+    // max keeps the lowest index on ties.
     const int vw = v0 + wm * kWaveM;
     const bool ragged = vw + kWaveM > a.V;
 #pragma unroll
     for (int mi = 0; mi < kMI; mi++) {
       float sb[16];
+      if constexpr (HAS_BIAS) {
 #pragma unroll
-      for (int g = 0; g < 4; g++) {
-        float b4[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (HAS_BIAS)
-          load_bias4<T>(reinterpret_cast<const T*>(a.bias), vw + mi * 32 + 8 * g + 4 * (lane >> 5), a.V, b4);
+        for (int g = 0; g < 4; g++) {
+          float b4[4];
+          lds_vec4<T>(bias_tile, wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5), b4);
 #pragma unroll
-        for (int j = 0; j < 4; j++) sb[4 * g + j] = a.scale * b4[j];
+          for (int j = 0; j < 4; j++) sb[4 * g + j] = a.scale * b4[j];
+        }
       }
 #pragma unroll
       for (int ni = 0; ni < kNI; ni++) {
         float z[16];
-        float mx = kMasked;
-        int ix = 0;
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           float v = HAS_BIAS ? fmaf(acc[mi][ni][r], a.scale, sb[r]) : acc[mi][ni][r] * a.scale;
           if constexpr (SOFTCAP) v = softcap_apply(v, a.two_log2e_over_cap, a.cap, a.two_cap);
-          const int row = acc_row(mi, r, lane);
-          if (ragged && vw + row >= a.V) v = kMasked;
           z[r] = v;
-          if (v > mx) {
-            mx = v;
-            ix = row;
-          }
         }
+        if (ragged) {
+#pragma unroll
+          for (int r = 0; r < 16; r++)
+            if (vw + acc_row(mi, r, lane) >= a.V) z[r] = kMasked;
+        }
+        float mx = z[0];
+#pragma unroll
+        for (int r = 1; r < 16; r++) mx = fmaxf(mx, z[r]);
         // the target logit, where some lane of the wave holds its row here
         const int rel = tgt[ni] - vw - mi * 32;
         const bool hit = rel >= 0 && rel < 32 && (((rel >> 2) & 1) == (lane >> 5));
@@ -162,8 +157,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
             if (acc_row(0, r, lane) == rel) st[ni].zt = z[r];
         }
         const float m_old = st[ni].m;
+        if (mx > m_old) {   // a new running max: its lowest row in this block
+          int ix = 0;
+#pragma unroll
+          for (int r = 15; r >= 0; r--)
+            if (z[r] == mx) ix = acc_row(mi, r, lane);
+          st[ni].idx = vw + ix;
+        }
         const float m_new = fmaxf(m_old, mx);
-        if (mx > m_old) st[ni].idx = vw + ix;
         const float mL = m_new * kLog2e;
         const float alpha = fast_exp2(fmaf(m_old, kLog2e, -mL));
         float se0 = 0.f, se1 = 0.f, sz0 = 0.f, sz1 = 0.f;
