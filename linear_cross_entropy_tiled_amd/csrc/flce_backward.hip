@@ -102,12 +102,6 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
-template <typename T>
-__device__ __forceinline__ void load_bias4_bwd(const T* b, int r0, int V, float* out) {
-#pragma unroll
-  for (int j = 0; j < 4; j++) out[j] = (r0 + j < V) ? load_elem<T>(b, r0 + j) : 0.0f;
-}
-
 // ---------------------------------------------------------------------------
 // dlogits: one 256 (vocab) x 256 (token) tile per workgroup.
 // ---------------------------------------------------------------------------
@@ -155,6 +149,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
   db.k_bytes = a.H * E;
   const int KT = (a.H * E + kBKB - 1) / kBKB;
 
+  // per-token coefficients (coefA, coefB, lseL, target) of the 256 tokens
+  // and the bias of the 256 vocabulary rows, staged in LDS by DMA; the main
+  // loop's first stage wait covers them
+  static __shared__ __attribute__((aligned(16))) char vec_lds[4 * 1024 + 256 * sizeof(T)];
+  {
+    const uint32_t tok_bytes = 1024;   // the per-token arrays hold N_pad (a multiple of 256) entries
+    if (wave == 0) dma_vector(a.coefA + t0, tok_bytes, vec_lds, 1024, lane);
+    if (wave == 1) dma_vector(a.coefB + t0, tok_bytes, vec_lds + 1024, 1024, lane);
+    if (wave == 2) dma_vector(a.lseL + t0, tok_bytes, vec_lds + 2048, 1024, lane);
+    if (wave == 3) dma_vector(a.tgt + t0, tok_bytes, vec_lds + 3072, 1024, lane);
+    // rounded up to whole words: an odd last bf16 entry shares its word
+    // (same page) with a masked row
+    if (HAS_BIAS && wave == 4)
+      dma_vector(reinterpret_cast<const T*>(a.bias) + v0, ((uint32_t)max(min(a.V - v0, 256), 0) * E + 3u) & ~3u,
+                 vec_lds + 4096, 256 * E, lane);
+  }
+
   f32x16 acc[kMI][kNI];
   zero_acc(acc);
   tile_mainloop<T, true, true>(da, db, KT, grouped_share(vt, tt), acc);
@@ -165,15 +176,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
   // over this tile's 256 tokens for grad_bias
   const int vw = v0 + wm * kWaveM;
   const bool ragged = vw + kWaveM > a.V;
-  float cA[kNI], cB[kNI], lL[kNI];
+  // softcap'(z) = 1 - (z/cap)^2
+  const float k2 = SOFTCAP ? -1.0f / (a.cap * a.cap) : 0.0f;
+  float cAs[kNI], cBs[kNI], lL[kNI];
   int rel[kNI];
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
-    const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
-    cA[ni] = a.coefA[t];
-    cB[ni] = a.coefB[t];
-    lL[ni] = a.lseL[t];
-    rel[ni] = a.tgt[t] - vw;
+    const int tl = wn * kWaveN + ni * 32 + (lane & 31);
+    cAs[ni] = reinterpret_cast<const float*>(vec_lds)[tl] * a.scale;
+    cBs[ni] = reinterpret_cast<const float*>(vec_lds + 1024)[tl] * a.scale;
+    lL[ni] = reinterpret_cast<const float*>(vec_lds + 2048)[tl];
+    rel[ni] = reinterpret_cast<const int*>(vec_lds + 3072)[tl] - vw;
   }
   T* D = reinterpret_cast<T*>(a.D);
   float* xs = reinterpret_cast<float*>(g_stage0);   // [wm][wn][mi][64 lanes]: per-wave column sums
@@ -181,33 +194,45 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
 #pragma unroll
   for (int mi = 0; mi < kMI; mi++) {
     float sb[16];
+    if constexpr (HAS_BIAS) {
 #pragma unroll
-    for (int g = 0; g < 4; g++) {
-      float b4[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (HAS_BIAS)
-        load_bias4_bwd<T>(reinterpret_cast<const T*>(a.bias), vw + mi * 32 + 8 * g + 4 * (lane >> 5), a.V, b4);
+      for (int g = 0; g < 4; g++) {
+        float b4[4];
+        lds_vec4<T>(vec_lds + 4096, wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5), b4);
 #pragma unroll
-      for (int j = 0; j < 4; j++) sb[4 * g + j] = a.scale * b4[j];
+        for (int j = 0; j < 4; j++) sb[4 * g + j] = a.scale * b4[j];
+      }
     }
     float cs[16];
 #pragma unroll
     for (int r = 0; r < 16; r++) cs[r] = 0.0f;
 #pragma unroll
     for (int ni = 0; ni < kNI; ni++) {
-      float d[16];
+      float z[16], d[16];
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        float z = HAS_BIAS ? fmaf(acc[mi][ni][r], a.scale, sb[r]) : acc[mi][ni][r] * a.scale;
-        if constexpr (SOFTCAP) z = softcap_apply(z, a.two_log2e_over_cap, a.cap, a.two_cap);
-        const int row = acc_row(mi, r, lane);
-        const float p = fast_exp2(fmaf(z, kLog2e, -lL[ni]));
-        float v = fmaf(cA[ni], p, row == rel[ni] ? -cB[ni] : 0.0f);
-        if constexpr (SOFTCAP) v *= fmaf(z * z, a.neg_scale_over_cap2, a.scale);
-        else v *= a.scale;
-        if (ragged && vw + row >= a.V) v = 0.0f;
-        d[r] = v;
-        cs[r] += v;
+        float zz = HAS_BIAS ? fmaf(acc[mi][ni][r], a.scale, sb[r]) : acc[mi][ni][r] * a.scale;
+        if constexpr (SOFTCAP) zz = softcap_apply(zz, a.two_log2e_over_cap, a.cap, a.two_cap);
+        z[r] = zz;
+        const float p = fast_exp2(fmaf(zz, kLog2e, -lL[ni]));
+        if constexpr (SOFTCAP) d[r] = p * fmaf(zz * zz, cAs[ni] * k2, cAs[ni]);
+        else d[r] = p * cAs[ni];
       }
+      // the target row, where some lane of the wave holds it here
+      const int rt = rel[ni] - mi * 32;
+      const bool hit = rt >= 0 && rt < 32 && (((rt >> 2) & 1) == (lane >> 5));
+      if (__builtin_amdgcn_ballot_w64(hit)) {
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+          if (acc_row(0, r, lane) == rt) d[r] -= SOFTCAP ? cBs[ni] * fmaf(z[r] * z[r], k2, 1.0f) : cBs[ni];
+      }
+      if (ragged) {
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+          if (vw + acc_row(mi, r, lane) >= a.V) d[r] = 0.0f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r++) cs[r] += d[r];
       const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
       T* drow = D + (size_t)t * a.ldD + (vw - a.cv0) + mi * 32 + 4 * (lane >> 5);
 #pragma unroll
