@@ -62,7 +62,8 @@ constexpr int kWaveM = 32 * kMI, kWaveN = 32 * kNI;   // 128 x 64
 constexpr int kOperandStage = kBM * kBKB;           // one operand's stage: 32 KiB
 constexpr int kStageBytes = 2 * kOperandStage;      // A + B: 64 KiB
 constexpr int kMainLds = 2 * kStageBytes;           // double buffer, 128 KiB
-constexpr int kBlocksPerWave = kOperandStage / 1024 / kWaves;   // 1 KiB DMA blocks per wave per operand
+constexpr int kLoadWaves = kWaves / 2;                          // waves that issue the stage loads
+constexpr int kLoadBlocks = kOperandStage / 1024 / kLoadWaves;  // 1 KiB DMA blocks per loading wave per operand
 constexpr int kSubsteps = 4;
 constexpr uint32_t kOob = 0x80000000u;              // buffer offset that reads 0
 
@@ -243,11 +244,15 @@ struct OperandLoader {
     dma4_sink(rsrc, sink, active ? voff : kOob);
   }
 
-  // Issue this wave's direct-to-LDS loads of stage kt.
+  // Issue this wave's direct-to-LDS loads of stage kt.  Only the first half
+  // of the waves load (kLoadBlocks blocks each): the two waves that share a
+  // SIMD are not issued evenly (the older one, wm = 0, runs ahead and then
+  // waits at the stage barrier), so the loads go to the waves with slack.
   __device__ __forceinline__ void load(int kt, char* stage) const {
+    if (wave >= kLoadWaves) return;
 #pragma unroll
-    for (int i = 0; i < kBlocksPerWave; i++) {
-      const int b = wave * kBlocksPerWave + i;   // 1 KiB block of the stage; parity = parity of i
+    for (int i = 0; i < kLoadBlocks; i++) {
+      const int b = wave * kLoadBlocks + i;   // 1 KiB block of the stage; parity = parity of i
       uint32_t voff, soff;
       if constexpr (KMAJOR) {
         const uint32_t k0 = (uint32_t)kt * kBKB;
@@ -391,13 +396,15 @@ __device__ __forceinline__ bool prefetch_stage(const OperandLoader<T, A_KMAJOR>&
   if constexpr (sizeof(T) != 2) {
     return false;
   } else {
-    // waves 0-3 take A's lines, 64 each; waves 4-7 take B's
-    const bool is_a = wave < 4;
+    // the loading waves prefetch too: waves 0-1 take A's lines, waves 2-3
+    // B's, 64 each (a share of at most 128 lines: n >= 2)
+    if (wave >= kLoadWaves) return false;
+    const bool is_a = wave < kLoadWaves / 2;
     const int n = is_a ? sh.a_n : sh.b_n;
-    if (n <= 0) return false;
+    if (n < 2) return false;
     const int rank = is_a ? sh.a_rank : sh.b_rank;
     const int first = rank * 256 / n, count = (rank + 1) * 256 / n - first;
-    const int off = (wave & 3) * 64;
+    const int off = (wave % (kLoadWaves / 2)) * 64;
     if (off >= count) return false;
     const uint32_t sink = __builtin_amdgcn_readfirstlane(lds_addr_of(g_prefetch_sink));
     const bool active = off + lane < count;
