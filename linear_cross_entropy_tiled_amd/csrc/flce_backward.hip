@@ -176,16 +176,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
   // over this tile's 256 tokens for grad_bias
   const int vw = v0 + wm * kWaveM;
   const bool ragged = vw + kWaveM > a.V;
-  // softcap'(z) = 1 - (z/cap)^2
-  const float k2 = SOFTCAP ? -1.0f / (a.cap * a.cap) : 0.0f;
-  float cAs[kNI], cBs[kNI], lL[kNI];
+  // With the cap, everything is written in r = 1 / (exp(2v/cap) + 1), where v
+  // is the scaled logit: z = cap (1 - 2r), softcap'(z) = 1 - (z/cap)^2 =
+  // 4 r (1 - r) and p = exp2(r * (-2 cap log2e) + cap log2e - LSE log2e).
+  // Per token: cAs = scale coefA (4x with the cap), cBs likewise, k0 = the
+  // exponent's constant term (or -LSE log2e without the cap).
+  const float s2 = SOFTCAP ? a.scale * a.two_log2e_over_cap : a.scale;   // scale folded into the exp argument
+  const float k1 = -a.two_cap * kLog2e;
+  const float cmul = SOFTCAP ? 4.0f * a.scale : a.scale;
+  float cAs[kNI], cBs[kNI], k0[kNI];
   int rel[kNI];
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
     const int tl = wn * kWaveN + ni * 32 + (lane & 31);
-    cAs[ni] = reinterpret_cast<const float*>(vec_lds)[tl] * a.scale;
-    cBs[ni] = reinterpret_cast<const float*>(vec_lds + 1024)[tl] * a.scale;
-    lL[ni] = reinterpret_cast<const float*>(vec_lds + 2048)[tl];
+    cAs[ni] = reinterpret_cast<const float*>(vec_lds)[tl] * cmul;
+    cBs[ni] = reinterpret_cast<const float*>(vec_lds + 1024)[tl] * cmul;
+    const float lL = reinterpret_cast<const float*>(vec_lds + 2048)[tl];
+    k0[ni] = SOFTCAP ? fmaf(a.cap, kLog2e, -lL) : -lL;
     rel[ni] = reinterpret_cast<const int*>(vec_lds + 3072)[tl] - vw;
   }
   T* D = reinterpret_cast<T*>(a.D);
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
         float b4[4];
         lds_vec4<T>(vec_lds + 4096, wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5), b4);
 #pragma unroll
-        for (int j = 0; j < 4; j++) sb[4 * g + j] = a.scale * b4[j];
+        for (int j = 0; j < 4; j++) sb[4 * g + j] = s2 * b4[j];
       }
     }
     float cs[16];
@@ -208,15 +215,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
     for (int r = 0; r < 16; r++) cs[r] = 0.0f;
 #pragma unroll
     for (int ni = 0; ni < kNI; ni++) {
-      float z[16], d[16];
+      float f[16], d[16];   // f: softcap' / 4 with the cap, else unused
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        float zz = HAS_BIAS ? fmaf(acc[mi][ni][r], a.scale, sb[r]) : acc[mi][ni][r] * a.scale;
-        if constexpr (SOFTCAP) zz = softcap_apply(zz, a.two_log2e_over_cap, a.cap, a.two_cap);
-        z[r] = zz;
-        const float p = fast_exp2(fmaf(zz, kLog2e, -lL[ni]));
-        if constexpr (SOFTCAP) d[r] = p * fmaf(zz * zz, cAs[ni] * k2, cAs[ni]);
-        else d[r] = p * cAs[ni];
+        const float v = HAS_BIAS ? fmaf(acc[mi][ni][r], s2, sb[r]) : acc[mi][ni][r] * s2;
+        if constexpr (SOFTCAP) {
+          const float rr = fast_rcp(fast_exp2(v) + 1.0f);
+          const float p = fast_exp2(fmaf(rr, k1, k0[ni]));
+          f[r] = fmaf(-rr, rr, rr);
+          d[r] = (p * cAs[ni]) * f[r];
+        } else {
+          d[r] = fast_exp2(fmaf(v, kLog2e, k0[ni])) * cAs[ni];
+        }
       }
       // the target row, where some lane of the wave holds it here
       const int rt = rel[ni] - mi * 32;
@@ -224,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
       if (__builtin_amdgcn_ballot_w64(hit)) {
 #pragma unroll
         for (int r = 0; r < 16; r++)
-          if (acc_row(0, r, lane) == rt) d[r] -= SOFTCAP ? cBs[ni] * fmaf(z[r] * z[r], k2, 1.0f) : cBs[ni];
+          if (acc_row(0, r, lane) == rt) d[r] -= SOFTCAP ? cBs[ni] * f[r] : cBs[ni];
       }
       if (ragged) {
 #pragma unroll

@@ -94,6 +94,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   // barriers of the tile in between, i.e. finished reading the older one)
   static __shared__ __attribute__((aligned(16))) char bias_lds[2][256 * sizeof(T)];
 
+  // scale of the accumulator into u (see the epilogue) and the exponent slope in r
+  const float s_u = SOFTCAP ? a.scale * a.two_log2e_over_cap : a.scale;
+  const float k1 = -a.two_cap * kLog2e;
+
   f32x16 acc[kMI][kNI];
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int v0 = vt * 256;
@@ -117,6 +121,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
     // running state of its token column.  Rows are visited in ascending
     // order, so taking an index only on a strict improvement of the running
     // max keeps the lowest index on ties.
+    //
+    // With the cap, the per-element work is written in u = 2 v log2(e) / cap
+    // (v the scaled logit) and r = 1 / (2^u + 1): z = cap (1 - 2r) rises with
+    // u, so the block max and argmax are taken on u; e^(z - m) =
+    // 2^(r (-2 cap log2e) + (cap - m) log2e); and sum e z = cap sum e -
+    // 2 cap sum e r.  Without the cap, u = z.
     const int vw = v0 + wm * kWaveM;
     const bool ragged = vw + kWaveM > a.V;
 #pragma unroll
@@ -128,57 +138,78 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
           float b4[4];
           lds_vec4<T>(bias_tile, wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5), b4);
 #pragma unroll
-          for (int j = 0; j < 4; j++) sb[4 * g + j] = a.scale * b4[j];
+          for (int j = 0; j < 4; j++) sb[4 * g + j] = s_u * b4[j];
         }
       }
 #pragma unroll
       for (int ni = 0; ni < kNI; ni++) {
-        float z[16];
+        float u[16], rr[16];
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-          float v = HAS_BIAS ? fmaf(acc[mi][ni][r], a.scale, sb[r]) : acc[mi][ni][r] * a.scale;
-          if constexpr (SOFTCAP) v = softcap_apply(v, a.two_log2e_over_cap, a.cap, a.two_cap);
-          z[r] = v;
+          u[r] = HAS_BIAS ? fmaf(acc[mi][ni][r], s_u, sb[r]) : acc[mi][ni][r] * s_u;
+          if constexpr (SOFTCAP) rr[r] = fast_rcp(fast_exp2(u[r]) + 1.0f);
         }
         if (ragged) {
 #pragma unroll
           for (int r = 0; r < 16; r++)
-            if (vw + acc_row(mi, r, lane) >= a.V) z[r] = kMasked;
+            if (vw + acc_row(mi, r, lane) >= a.V) {
+              u[r] = kMasked;
+              if constexpr (SOFTCAP) rr[r] = 1e30f;   // e = 2^(-huge) = 0, and e r = 0
+            }
         }
-        float mx = z[0];
+        float mu = u[0];
 #pragma unroll
-        for (int r = 1; r < 16; r++) mx = fmaxf(mx, z[r]);
+        for (int r = 1; r < 16; r++) mu = fmaxf(mu, u[r]);
+        // the block max in z; a block that is all masked rows keeps kMasked
+        float mx = mu;
+        if constexpr (SOFTCAP) mx = mu == kMasked ? kMasked : fmaf(-a.two_cap, fast_rcp(fast_exp2(mu) + 1.0f), a.cap);
         // the target logit, where some lane of the wave holds its row here
         const int rel = tgt[ni] - vw - mi * 32;
         const bool hit = rel >= 0 && rel < 32 && (((rel >> 2) & 1) == (lane >> 5));
         if (__builtin_amdgcn_ballot_w64(hit)) {
 #pragma unroll
           for (int r = 0; r < 16; r++)
-            if (acc_row(0, r, lane) == rel) st[ni].zt = z[r];
+            if (acc_row(0, r, lane) == rel) st[ni].zt = SOFTCAP ? fmaf(-a.two_cap, rr[r], a.cap) : u[r];
         }
         const float m_old = st[ni].m;
         if (mx > m_old) {   // a new running max: its lowest row in this block
           int ix = 0;
 #pragma unroll
           for (int r = 15; r >= 0; r--)
-            if (z[r] == mx) ix = acc_row(mi, r, lane);
+            if (u[r] == mu) ix = acc_row(mi, r, lane);
           st[ni].idx = vw + ix;
         }
         const float m_new = fmaxf(m_old, mx);
         const float mL = m_new * kLog2e;
         const float alpha = fast_exp2(fmaf(m_old, kLog2e, -mL));
         float se0 = 0.f, se1 = 0.f, sz0 = 0.f, sz1 = 0.f;
+        if constexpr (SOFTCAP) {
+          // here sz accumulates sum e r
+          const float k0 = fmaf(a.cap, kLog2e, -mL);
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float e0 = fast_exp2(fmaf(z[r], kLog2e, -mL));
-          const float e1 = fast_exp2(fmaf(z[r + 1], kLog2e, -mL));
-          se0 += e0;
-          se1 += e1;
-          sz0 = fmaf(e0, z[r], sz0);
-          sz1 = fmaf(e1, z[r + 1], sz1);
+          for (int r = 0; r < 16; r += 2) {
+            const float e0 = fast_exp2(fmaf(rr[r], k1, k0));
+            const float e1 = fast_exp2(fmaf(rr[r + 1], k1, k0));
+            se0 += e0;
+            se1 += e1;
+            sz0 = fmaf(e0, rr[r], sz0);
+            sz1 = fmaf(e1, rr[r + 1], sz1);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float e0 = fast_exp2(fmaf(u[r], kLog2e, -mL));
+            const float e1 = fast_exp2(fmaf(u[r + 1], kLog2e, -mL));
+            se0 += e0;
+            se1 += e1;
+            sz0 = fmaf(e0, u[r], sz0);
+            sz1 = fmaf(e1, u[r + 1], sz1);
+          }
         }
-        st[ni].l = fmaf(st[ni].l, alpha, se0 + se1);
-        st[ni].T = fmaf(st[ni].T, alpha, sz0 + sz1);
+        const float se = se0 + se1;
+        const float sz = SOFTCAP ? fmaf(-a.two_cap, sz0 + sz1, a.cap * se) : sz0 + sz1;
+        st[ni].l = fmaf(st[ni].l, alpha, se);
+        st[ni].T = fmaf(st[ni].T, alpha, sz);
         st[ni].m = m_new;
       }
     }
