@@ -295,3 +295,17 @@ def _sampled_check(flce, wl: si.Workload, n_rows=512, n_vocab=512):
                                   "bf16_n8192_h4096_v32000_zipf"])
 def test_full_size_sampled(flce_lib, name):
     _sampled_check(flce_lib, si.WORKLOADS[name])
+
+
+# Everything ragged at a mid size: N, H and V none a multiple of 256 (H = 1600
+# leaves a partial hidden tile in both gradient contractions), an odd V (the
+# bias staging rounds its last word), all options on, and the cap low enough
+# to bend the logits.
+RAGGED_MID = si.Workload("bf16_n6000_h1600_v50257_ragged", 6000, 1600, 50257, "bf16", 0.02, 0.1,
+                         logit_scale=0.8, softcap=5.0, z_loss=1e-4, ignore_frac=0.1, reduction="mean",
+                         seed=7)
+
+
+@pytest.mark.slow
+def test_ragged_mid_size_sampled(flce_lib):
+    _sampled_check(flce_lib, RAGGED_MID)
