@@ -13,6 +13,9 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Scratch budget for the dlogits chunk (N_pad x Vc elements).
 static constexpr size_t kDlogitsBudget = size_t(512) << 20;
 static constexpr int64_t kMaxChunkTiles = 128;
+// grad_hidden K splits: at least this many 64-row stages each, partials within this budget
+static constexpr int64_t kMinStagesPerPart = 8;
+static constexpr size_t kGhPartBudget = size_t(256) << 20;
 // Number of compute units the forward split count is sized for (MI355X).
 static constexpr int64_t kTargetWorkgroups = 256;
 
@@ -76,6 +79,21 @@ int make_plan(const flce_params* p, Plan* pl) {
   P.Vc = tiles_per_chunk * 256;
   if (P.Vc * P.H * esize >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
   if (P.N_pad * P.Vc * esize >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+  // grad_hidden has only n_ht x n_tt output tiles; when that is well under one
+  // workgroup per CU, split each chunk's contraction (K = vocabulary rows) and
+  // add the fp32 partials in a fixed order afterwards
+  {
+    const int64_t tiles = P.n_ht * P.n_tt;
+    const int64_t stages = P.Vc * esize / 128;   // K stages of 128 bytes per row
+    int64_t parts = tiles > 0 ? (kTargetWorkgroups + tiles - 1) / tiles : 1;
+    if (parts > stages / kMinStagesPerPart) parts = stages / kMinStagesPerPart;
+    const int64_t per_part_bytes = P.N * P.H * 4;
+    if (per_part_bytes > 0 && parts > (int64_t)(kGhPartBudget / per_part_bytes))
+      parts = (int64_t)(kGhPartBudget / per_part_bytes);
+    if (parts < 2 || tiles >= kTargetWorkgroups / 2) parts = 1;
+    P.gh_kt_per_part = (int)((stages + parts - 1) / parts);
+    P.gh_parts = (int)((stages + P.gh_kt_per_part - 1) / P.gh_kt_per_part);
+  }
   size_t o = kStatusBytes;
   P.b_coefA = o;
   o = align_up(o + size_t(P.N_pad) * 4, 256);
@@ -91,6 +109,8 @@ int make_plan(const flce_params* p, Plan* pl) {
   o = align_up(o + size_t(P.N_pad) * P.H * esize, 256);
   P.b_ghacc = o;
   if (P.dtype == FLCE_BF16 && P.n_chunks > 1) o = align_up(o + size_t(P.N) * P.H * 4, 256);
+  P.b_ghpart = o;
+  if (P.gh_parts > 1) o = align_up(o + size_t(P.gh_parts) * P.N * P.H * 4, 256);
   P.b_gbpart = o;
   o = align_up(o + size_t(P.n_tt) * P.V_pad * 4, 256);
   P.b_bytes = o;

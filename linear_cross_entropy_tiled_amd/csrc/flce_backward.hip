@@ -368,34 +368,46 @@ struct GhArgs {
   void* out;
   int out_f32;
   int mode;
+  int parts;        // > 1: K split; split p covers stages [p kt_per_part, (p+1) kt_per_part)
+  int kt_per_part;
+  float* part;      // parts x N x H fp32 partials (parts > 1)
 };
 
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void bwd_gh_kernel(GhArgs a) {
   constexpr int E = sizeof(T);
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  // the split is the slow index, so the workgroups one XCD runs together
+  // share a K range and the grouped tile order still applies within it
+  const int n_tiles = a.n_ht * a.n_tt;
+  const int split = L / n_tiles;
   int ht, tt;
-  grouped_tile(L, a.n_ht, a.n_tt, 4, ht, tt);
+  grouped_tile(L - split * n_tiles, a.n_ht, a.n_tt, 4, ht, tt);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int h0 = ht * 256, t0 = tt * 256;
 
-  OperandDesc da;     // weight rows v (K) of the chunk, columns h: transposing reads
+  // this split's K range: stages [kt0, kt0 + KT) of the chunk (64 vocabulary rows each)
+  const int KT_all = (a.cvn * E + kBKB - 1) / kBKB;
+  const int kt0 = split * a.kt_per_part;
+  const int KT = max(min(KT_all - kt0, a.kt_per_part), 0);
+  const int v_off = kt0 * (kBKB / E);   // first vocabulary row of the split within the chunk
+
+  OperandDesc da;     // weight rows v (K) of the split, columns h: transposing reads
   const uint32_t ldw = (uint32_t)a.H * E;
-  const int vrows = min(a.V - a.cv0, a.cvn);
-  da.base = a.weight + ((size_t)a.cv0 * a.H + h0) * E;
+  const int vrows = max(min(a.V - a.cv0, a.cvn) - v_off, 0);
+  da.base = a.weight + ((size_t)(a.cv0 + v_off) * a.H + h0) * E;
   da.ld_bytes = ldw;
-  da.nrec = (uint32_t)((size_t)vrows * ldw - (size_t)h0 * E);
+  da.nrec = vrows > 0 ? (uint32_t)((size_t)vrows * ldw - (size_t)h0 * E) : 0u;
   da.cols_valid = a.H - h0;
   da.k_bytes = 0;
   OperandDesc db;     // dlogits rows t, K = v
   const uint32_t ldd = (uint32_t)a.ldD * E;
-  db.base = a.D + (size_t)t0 * ldd;
+  db.base = a.D + (size_t)t0 * ldd + (size_t)v_off * E;
   db.ld_bytes = ldd;
-  db.nrec = 256u * ldd;
+  db.nrec = 256u * ldd - (uint32_t)v_off * E;
   db.cols_valid = 0;
-  db.k_bytes = a.cvn * E;
-  const int KT = (a.cvn * E + kBKB - 1) / kBKB;
+  db.k_bytes = (a.cvn - v_off) * E;
 
   f32x16 acc[kMI][kNI];
   zero_acc(acc);
@@ -414,6 +426,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gh_kernel(GhArgs a) {
         const size_t o = (size_t)t * a.H + h;
         float c0 = acc[mi][ni][4 * g], c1 = acc[mi][ni][4 * g + 1];
         float c2 = acc[mi][ni][4 * g + 2], c3 = acc[mi][ni][4 * g + 3];
+        if (a.parts > 1) {   // partial of this split; bwd_gh_reduce applies the mode
+          store4(a.part + (size_t)split * a.N * a.H + o, c0, c1, c2, c3);
+          continue;
+        }
         if (a.mode == 1 || a.mode == 2) {
           const f32x4 prev = *reinterpret_cast<const f32x4*>(a.accb + o);
           c0 += prev[0];
@@ -428,6 +444,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gh_kernel(GhArgs a) {
           store4(reinterpret_cast<bf16*>(a.out) + o, c0, c1, c2, c3);
         }
       }
+  }
+}
+
+// grad_hidden with a K split: out = (mode 1, 2: accumulator +) sum of the
+// partials in split order, stored like bwd_gh_kernel's epilogue (mode 0, 1 ->
+// accumulator; 2, 3 -> output, cast).  Four consecutive elements per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_gh_reduce(const float* part, int parts, int64_t n4, int64_t stride,
+                                                     float* accb, void* out, int out_f32, int mode) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 s = (mode == 1 || mode == 2) ? reinterpret_cast<const f32x4*>(accb)[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < parts; p++) s += reinterpret_cast<const f32x4*>(part + (size_t)p * stride)[i];
+  if (mode <= 1 || out_f32) {
+    float* dst = mode <= 1 ? accb : reinterpret_cast<float*>(out);
+    reinterpret_cast<f32x4*>(dst)[i] = s;
+  } else {
+    store4(reinterpret_cast<T*>(out) + 4 * i, s[0], s[1], s[2], s[3]);
   }
 }
 
@@ -567,7 +601,15 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       h.out = grad_hidden;
       h.out_f32 = gh_f32;
       h.mode = pl.n_chunks == 1 ? 3 : (c == 0 ? 0 : (c == pl.n_chunks - 1 ? 2 : 1));
-      bwd_gh_kernel<T><<<(int)(pl.n_ht * pl.n_tt), kThreads, 0, st>>>(h);
+      h.parts = pl.gh_parts;
+      h.kt_per_part = pl.gh_kt_per_part;
+      h.part = reinterpret_cast<float*>(ws + pl.b_ghpart);
+      bwd_gh_kernel<T><<<(int)(pl.n_ht * pl.n_tt) * pl.gh_parts, kThreads, 0, st>>>(h);
+      if (pl.gh_parts > 1) {
+        const int64_t n4 = pl.N * pl.H / 4;
+        bwd_gh_reduce<T><<<(int)((n4 + 255) / 256), 256, 0, st>>>(h.part, pl.gh_parts, n4, pl.N * pl.H, accb,
+                                                                  grad_hidden, gh_f32, h.mode);
+      }
     }
   }
   if (grad_bias) {

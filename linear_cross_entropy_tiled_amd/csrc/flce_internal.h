@@ -27,7 +27,9 @@ struct Plan {
   // backward
   int64_t Vc;                    // vocabulary chunk width (multiple of 256)
   int n_chunks;
-  size_t b_coefA, b_coefB, b_lseL, b_tgt, b_D, b_xt, b_ghacc, b_gbpart, b_bytes;
+  int gh_parts;                  // grad_hidden: K (vocabulary) splits per chunk when there are few output tiles
+  int gh_kt_per_part;            // 64-row stages per split
+  size_t b_coefA, b_coefB, b_lseL, b_tgt, b_D, b_xt, b_ghacc, b_ghpart, b_gbpart, b_bytes;
 };
 
 constexpr size_t kStatusBytes = 256;   // status word at workspace offset 0
