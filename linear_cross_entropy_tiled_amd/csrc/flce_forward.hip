@@ -294,15 +294,24 @@ __global__ __launch_bounds__(256) void fwd_finalize_rows(FinArgs a) {
     r.T = a.part_T[i];
     r.zt = a.part_zt[i];
     r.idx = a.part_idx[i];
-    for (int s = 1; s < a.S; s++) {
-      const size_t o = (size_t)s * a.N_pad + i;
-      RowState q;
-      q.m = a.part_m[o];
-      q.l = a.part_l[o];
-      q.T = a.part_T[o];
-      q.zt = a.part_zt[o];
-      q.idx = a.part_idx[o];
-      merge_state(r, q);
+    // splits merged in index order; their partials are loaded 8 at a time so
+    // that the loads do not wait on each other
+    for (int s0 = 1; s0 < a.S; s0 += 8) {
+      RowState q[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        if (s0 + j < a.S) {
+          const size_t o = (size_t)(s0 + j) * a.N_pad + i;
+          q[j].m = a.part_m[o];
+          q[j].l = a.part_l[o];
+          q[j].T = a.part_T[o];
+          q[j].zt = a.part_zt[o];
+          q[j].idx = a.part_idx[o];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        if (s0 + j < a.S) merge_state(r, q[j]);
     }
     const float lse = r.m + fast_log2(r.l) * kLn2;
     const float ent = lse - r.T / r.l;
