@@ -299,15 +299,13 @@ __global__ __launch_bounds__(256) void fwd_finalize_rows(FinArgs a) {
     for (int s0 = 1; s0 < a.S; s0 += 8) {
       RowState q[8];
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        if (s0 + j < a.S) {
-          const size_t o = (size_t)(s0 + j) * a.N_pad + i;
-          q[j].m = a.part_m[o];
-          q[j].l = a.part_l[o];
-          q[j].T = a.part_T[o];
-          q[j].zt = a.part_zt[o];
-          q[j].idx = a.part_idx[o];
-        }
+      for (int j = 0; j < 8; j++) {   // past the last split: reload the last one (not merged)
+        const size_t o = (size_t)min(s0 + j, a.S - 1) * a.N_pad + i;
+        q[j].m = a.part_m[o];
+        q[j].l = a.part_l[o];
+        q[j].T = a.part_T[o];
+        q[j].zt = a.part_zt[o];
+        q[j].idx = a.part_idx[o];
       }
 #pragma unroll
       for (int j = 0; j < 8; j++)
