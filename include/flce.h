@@ -45,7 +45,11 @@ extern "C" {
 typedef enum {
   FLCE_OK = 0,
   FLCE_ERR_INVALID_ARG = -1,          /* NULL required pointer, negative size, bad enum      */
-  FLCE_ERR_UNSUPPORTED = -2,          /* H % 8 != 0, misaligned pointer, too large a problem */
+  FLCE_ERR_UNSUPPORTED = -2,          /* H % 8 != 0, misaligned pointer, or too large: the
+                                         kernels use 32-bit offsets, so N*H*elem and the
+                                         backward's (vocabulary chunk, <= 32768 rows) x H
+                                         and N x chunk must stay under 2^31 bytes, N and V
+                                         under 2^30, H under 2^20                             */
   FLCE_ERR_WORKSPACE_TOO_SMALL = -3,
   FLCE_ERR_HIP = -4,                  /* a HIP runtime call failed                           */
   FLCE_ERR_TARGET_OUT_OF_RANGE = -5   /* reported by flce_get_status only                    */
