@@ -110,7 +110,7 @@ struct DlogitsArgs {
   const char* weight;
   const void* bias;
   int N, H, V;
-  float scale, cap, two_log2e_over_cap, two_cap, neg_scale_over_cap2;
+  float scale, cap, two_log2e_over_cap, two_cap;
   int cv0;          // first vocabulary row of the chunk
   int n_vt_c;       // vocabulary tiles in the chunk
   int n_tt;
@@ -548,7 +548,6 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       d.cap = pl.cap;
       d.two_log2e_over_cap = pl.cap > 0 ? 2.0f * kLog2e / pl.cap : 0.0f;
       d.two_cap = 2.0f * pl.cap;
-      d.neg_scale_over_cap2 = pl.cap > 0 ? -pl.scale / (pl.cap * pl.cap) : 0.0f;
       d.cv0 = cv0;
       d.n_vt_c = n_vt_c;
       d.n_tt = (int)pl.n_tt;
