@@ -68,6 +68,13 @@ def measured_traffic(workload: str):
         return None
 
 
+def _device_info(torch):
+    """Name, compute units and architecture of the GPU as the runtime reports them (the peak assumes 256 CUs)."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "compute_units": p.multi_processor_count,
+            "arch": getattr(p, "gcnArchName", ""), "memory_gib": round(p.total_memory / 2**30, 1)}
+
+
 def _to_dev(inp, dtype):
     import torch
     def dev(a):
@@ -213,6 +220,7 @@ def main():
         "fwd_tflops": fwd_tflops,
         "bwd_tflops": bwd_tflops,
         "peak_mem_gib": torch.cuda.max_memory_allocated() / 2**30,
+        "device": _device_info(torch),
         # the forward call is the vocabulary-tiled logit kernel plus two small
         # finalize kernels; its HIP-event time bounds the tile kernel's time
         "roofline": {"bound": "mfma", "kernel": "fwd_tiles_kernel (+ finalize)",
