@@ -27,7 +27,8 @@
  *    workspaces may run concurrently.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = default stream).
  *    flce_forward and flce_backward never synchronise the host.
- *  - Every output is overwritten, never accumulated into.
+ *  - Every output is overwritten, except grad_weight / grad_bias when
+ *    params->flags asks the backward pass to accumulate into them.
  *  - Arguments are validated on the host before anything is enqueued; a
  *    non-zero status means nothing was launched.
  *  - Results are deterministic: the same inputs give the same bits, run to run.
@@ -65,6 +66,17 @@ typedef enum {
 
 typedef enum { FLCE_PASS_FORWARD = 0, FLCE_PASS_BACKWARD = 1 } flce_pass;
 
+/* flce_params.flags: the backward pass adds its result to what the output
+ * buffer already holds instead of overwriting it, e.g. to accumulate the
+ * weight gradient over micro-batches without a separate add ("Chunked Linear
+ * Loss" page, "Weight-gradient accumulation dtype": accumulate in the weight
+ * dtype, or in fp32 with grad_weight_dtype = FLCE_F32).  The sum is formed in
+ * fp32 and rounded once to the buffer's dtype. */
+typedef enum {
+  FLCE_ACCUMULATE_GRAD_WEIGHT = 1,
+  FLCE_ACCUMULATE_GRAD_BIAS = 2
+} flce_flags;
+
 typedef struct {
   int64_t n_tokens;           /* N >= 0 (N = 0 is an empty batch)                        */
   int64_t hidden;             /* H >= 8, H % 8 == 0                                      */
@@ -73,7 +85,7 @@ typedef struct {
   int32_t dtype;              /* flce_dtype of hidden, weight and bias                   */
   int32_t grad_weight_dtype;  /* flce_dtype of grad_weight; accumulated in fp32 always   */
   int32_t reduction;          /* flce_reduction                                          */
-  int32_t reserved;           /* must be 0                                               */
+  int32_t flags;              /* flce_flags bits (backward only); 0 = overwrite outputs  */
   float logit_scale;          /* multiplies (x.W^T + b); 1.0 = off                       */
   float softcap;              /* cap of cap*tanh(v/cap); <= 0 = off                      */
   float z_loss;               /* z-loss multiplier lambda >= 0; 0 = off                  */

@@ -33,6 +33,8 @@ FLCE_BF16 = 1
 REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 FLCE_PASS_FORWARD = 0
 FLCE_PASS_BACKWARD = 1
+FLCE_ACCUMULATE_GRAD_WEIGHT = 1
+FLCE_ACCUMULATE_GRAD_BIAS = 2
 
 EXPORTED = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_get_status",
             "flce_status_string", "flce_version")
@@ -47,7 +49,7 @@ class flce_params(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("grad_weight_dtype", ctypes.c_int32),
         ("reduction", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("logit_scale", ctypes.c_float),
         ("softcap", ctypes.c_float),
         ("z_loss", ctypes.c_float),
@@ -139,7 +141,8 @@ def status_string(code: int) -> str:
 def make_params(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
                 grad_weight_dtype: Optional[str] = None, logit_scale: float = 1.0,
                 softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
-                reduction: str = "mean") -> flce_params:
+                reduction: str = "mean", accumulate_grad_weight: bool = False,
+                accumulate_grad_bias: bool = False) -> flce_params:
     if reduction not in REDUCTIONS:
         raise ValueError(f"invalid reduction {reduction!r}")
     dt = {"bf16": FLCE_BF16, "f32": FLCE_F32}
@@ -151,6 +154,8 @@ def make_params(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
     p.logit_scale = logit_scale
     p.softcap = softcap if softcap else 0.0
     p.z_loss = z_loss
+    p.flags = (FLCE_ACCUMULATE_GRAD_WEIGHT if accumulate_grad_weight else 0) | \
+              (FLCE_ACCUMULATE_GRAD_BIAS if accumulate_grad_bias else 0)
     return p
 
 
@@ -208,25 +213,36 @@ def forward(hidden, weight, targets, bias=None, *, logit_scale: float = 1.0,
 
 def backward(hidden, weight, targets, lse, grad_loss, bias=None, *, logit_scale: float = 1.0,
              softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
-             reduction: str = "mean", grad_weight_dtype: Optional[str] = None, workspace=None):
-    """Runs flce_backward on the current stream.  Returns (grad_hidden, grad_weight, grad_bias)."""
+             reduction: str = "mean", grad_weight_dtype: Optional[str] = None, workspace=None,
+             grad_weight=None, grad_bias=None):
+    """Runs flce_backward on the current stream.  Returns (grad_hidden, grad_weight, grad_bias).
+
+    If ``grad_weight`` (``grad_bias``) is given, the gradient is added to it in place (the
+    FLCE_ACCUMULATE_GRAD_WEIGHT / _BIAS flags) and the same tensor is returned."""
     import torch
     for t, n in ((hidden, "hidden"), (weight, "weight"), (targets, "targets"), (bias, "bias"),
-                 (lse, "lse"), (grad_loss, "grad_loss")):
+                 (lse, "lse"), (grad_loss, "grad_loss"), (grad_weight, "grad_weight"), (grad_bias, "grad_bias")):
         _check(t, n)
     n, h = hidden.shape
     v = weight.shape[0]
     dt = _dtype_name(hidden)
+    if grad_weight is not None:
+        grad_weight_dtype = _dtype_name(grad_weight)
+        if tuple(grad_weight.shape) != (v, h):
+            raise ValueError("grad_weight must have the weight's shape")
+    if grad_bias is not None and (bias is None or grad_bias.dtype != bias.dtype or grad_bias.numel() != v):
+        raise ValueError("grad_bias must match bias")
     p = make_params(n, h, v, dtype=dt, grad_weight_dtype=grad_weight_dtype, logit_scale=logit_scale,
-                    softcap=softcap, z_loss=z_loss, ignore_index=ignore_index, reduction=reduction)
+                    softcap=softcap, z_loss=z_loss, ignore_index=ignore_index, reduction=reduction,
+                    accumulate_grad_weight=grad_weight is not None, accumulate_grad_bias=grad_bias is not None)
     dev = hidden.device
     ws_bytes = flce_workspace_size(p, FLCE_PASS_BACKWARD)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
     gh = torch.empty((n, h), dtype=hidden.dtype, device=dev)
-    gw = torch.empty((v, h), dtype=tdt[grad_weight_dtype or dt], device=dev)
-    gb = torch.empty(v, dtype=bias.dtype, device=dev) if bias is not None else None
+    gw = grad_weight if grad_weight is not None else torch.empty((v, h), dtype=tdt[grad_weight_dtype or dt], device=dev)
+    gb = grad_bias if grad_bias is not None else (torch.empty(v, dtype=bias.dtype, device=dev) if bias is not None else None)
     rc = flce_backward(p, _ptr(hidden), _ptr(weight), _ptr(bias), _ptr(targets), _ptr(lse),
                        _ptr(grad_loss), _ptr(gh), _ptr(gw), _ptr(gb), _ptr(workspace),
                        workspace.numel(), _stream_handle(dev))

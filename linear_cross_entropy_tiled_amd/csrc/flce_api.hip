@@ -27,7 +27,8 @@ int make_plan(const flce_params* p, Plan* pl) {
   if (p->reduction != FLCE_REDUCTION_NONE && p->reduction != FLCE_REDUCTION_SUM &&
       p->reduction != FLCE_REDUCTION_MEAN)
     return FLCE_ERR_INVALID_ARG;
-  if (p->reserved != 0 || p->reserved_f != 0.0f) return FLCE_ERR_INVALID_ARG;
+  if ((p->flags & ~(FLCE_ACCUMULATE_GRAD_WEIGHT | FLCE_ACCUMULATE_GRAD_BIAS)) != 0 || p->reserved_f != 0.0f)
+    return FLCE_ERR_INVALID_ARG;
   if (!isfinite(p->logit_scale) || !isfinite(p->softcap) || !isfinite(p->z_loss) || p->z_loss < 0.0f)
     return FLCE_ERR_INVALID_ARG;
   if (p->hidden % 8 != 0) return FLCE_ERR_UNSUPPORTED;
@@ -46,6 +47,8 @@ int make_plan(const flce_params* p, Plan* pl) {
   P.dtype = p->dtype;
   P.gw_dtype = p->grad_weight_dtype;
   P.reduction = p->reduction;
+  P.accum_gw = (p->flags & FLCE_ACCUMULATE_GRAD_WEIGHT) != 0;
+  P.accum_gb = (p->flags & FLCE_ACCUMULATE_GRAD_BIAS) != 0;
   P.scale = p->logit_scale;
   P.cap = p->softcap > 0.0f ? p->softcap : 0.0f;
   P.z_loss = p->z_loss;

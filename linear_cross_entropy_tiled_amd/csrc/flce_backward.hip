@@ -102,6 +102,19 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// Four consecutive elements from global memory, widened to fp32.
+template <typename T> __device__ __forceinline__ void load4(const T* p, float* out);
+template <> __device__ __forceinline__ void load4<float>(const float* p, float* out) {
+  const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; j++) out[j] = v[j];
+}
+template <> __device__ __forceinline__ void load4<bf16>(const bf16* p, float* out) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; j++) out[j] = (float)v[j];
+}
+
 // ---------------------------------------------------------------------------
 // dlogits: one 256 (vocab) x 256 (token) tile per workgroup.
 // ---------------------------------------------------------------------------
@@ -296,6 +309,7 @@ struct GwArgs {
   int n_ht, n_vt_c;
   void* gw;
   int gw_f32;
+  int accumulate;   // add to grad_weight's current contents
 };
 
 template <typename T>
@@ -339,12 +353,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gw_kernel(GwArgs a) {
         const int h = h0 + wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5);
         if (h >= a.H) continue;
         const size_t o = (size_t)v * a.H + h;
+        float c[4] = {acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]};
+        if (a.accumulate) {
+          float prev[4];
+          if (a.gw_f32) load4<float>(reinterpret_cast<const float*>(a.gw) + o, prev);
+          else load4<bf16>(reinterpret_cast<const bf16*>(a.gw) + o, prev);
+#pragma unroll
+          for (int j = 0; j < 4; j++) c[j] += prev[j];
+        }
         if (a.gw_f32)
-          store4(reinterpret_cast<float*>(a.gw) + o, acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1],
-                 acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
+          store4(reinterpret_cast<float*>(a.gw) + o, c[0], c[1], c[2], c[3]);
         else
-          store4(reinterpret_cast<bf16*>(a.gw) + o, acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1],
-                 acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
+          store4(reinterpret_cast<bf16*>(a.gw) + o, c[0], c[1], c[2], c[3]);
       }
   }
 }
@@ -485,11 +505,13 @@ __global__ __launch_bounds__(256) void transpose_hidden_kernel(const T* x, int N
 
 // grad_bias[v] = sum over token tiles of the per-tile column sums, in order.
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_gb_reduce(const float* part, int n_tt, int ld, int V, T* gb) {
+__global__ __launch_bounds__(256) void bwd_gb_reduce(const float* part, int n_tt, int ld, int V, T* gb,
+                                                     int accumulate) {
   const int v = blockIdx.x * 256 + threadIdx.x;
   if (v >= V) return;
   float s = 0.0f;
   for (int i = 0; i < n_tt; i++) s += part[(size_t)i * ld + v];
+  if (accumulate) s += load_elem<T>(gb, v);
   gb[v] = (T)s;
 }
 
@@ -582,6 +604,7 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       g.n_vt_c = n_vt_c;
       g.gw = grad_weight;
       g.gw_f32 = pl.gw_dtype == FLCE_F32;
+      g.accumulate = pl.accum_gw ? 1 : 0;
       bwd_gw_kernel<T><<<(int)pl.n_ht * n_vt_c, kThreads, 0, st>>>(g);
     }
     if (pl.N > 0) {
@@ -613,7 +636,8 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
   }
   if (grad_bias) {
     bwd_gb_reduce<T><<<(int)((pl.V + 255) / 256), 256, 0, st>>>(gb_part, (int)pl.n_tt, (int)pl.V_pad,
-                                                               (int)pl.V, reinterpret_cast<T*>(grad_bias));
+                                                               (int)pl.V, reinterpret_cast<T*>(grad_bias),
+                                                               pl.accum_gb ? 1 : 0);
   }
   return hipGetLastError();
 }

@@ -14,6 +14,7 @@ struct Plan {
   int64_t N, H, V, ignore_index;
   int dtype, gw_dtype, reduction;
   bool has_bias;
+  bool accum_gw, accum_gb;       // backward adds into grad_weight / grad_bias
   float scale, cap, z_loss;
 
   int64_t n_tt, n_vt, n_ht;      // 256-wide tiles over tokens, vocabulary, hidden

@@ -70,7 +70,7 @@ def test_workspace_sizes(lib):
     ("dtype", 7, flce.FLCE_ERR_INVALID_ARG),
     ("grad_weight_dtype", 9, flce.FLCE_ERR_INVALID_ARG),
     ("reduction", 3, flce.FLCE_ERR_INVALID_ARG),
-    ("reserved", 1, flce.FLCE_ERR_INVALID_ARG),
+    ("flags", 4, flce.FLCE_ERR_INVALID_ARG),
     ("z_loss", -1.0, flce.FLCE_ERR_INVALID_ARG),
     ("logit_scale", float("inf"), flce.FLCE_ERR_INVALID_ARG),
 ])

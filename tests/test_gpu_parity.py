@@ -127,6 +127,37 @@ def _ws_probe(flce, d):
     return ws
 
 
+@pytest.mark.parametrize("gw_dtype", ["bf16", "f32"])
+def test_accumulate_into_grad_weight_and_bias(flce_lib, gw_dtype):
+    """FLCE_ACCUMULATE_GRAD_WEIGHT / _BIAS: the backward adds to the buffers' contents
+    (two vocabulary chunks, so every chunk's grad_weight rows take the add)."""
+    import torch
+    c = Case("accumulate", 300, 72, 33000, "bf16", 0.1, 0.8, 3.0, 1e-3, 0.1, "mean", gw_dtype,
+             weight_std=0.1, seed=21)
+    inp = _inputs(c)
+    d = to_device(inp, c.dtype)
+    loss, lse, _ = flce_lib.forward(d["hidden"], d["weight"], d["targets"], d["bias"], **_opts(c))
+    X, W, B, T = widened(inp, c.dtype)
+    _, rgh, rgw, rgb = oracle.forward_backward(X, W, B, T, inp["grad_loss"].astype(np.float64), **_opts(c))
+    # seeded prior contents on the gradients' scale (so that rounding the sum once stays
+    # inside the gradient tolerance), exactly representable in the buffers' dtypes
+    rng = np.random.default_rng(5)
+    sw, sb = np.abs(rgw).max() / 4, np.abs(rgb).max() / 4
+    gw0 = si.widen(si.round_to_bf16_bits(rng.normal(0, sw, (c.v, c.h)).astype(np.float32)), "bf16")
+    gb0 = si.widen(si.round_to_bf16_bits(rng.normal(0, sb, c.v).astype(np.float32)), "bf16")
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    gw_buf = torch.from_numpy(gw0.astype(np.float32)).to(tdt[gw_dtype]).cuda()
+    gb_buf = torch.from_numpy(gb0.astype(np.float32)).to(torch.bfloat16).cuda()
+    g = d["grad_loss"][:1]
+    gh, gw, gb = flce_lib.backward(d["hidden"], d["weight"], d["targets"], lse, g, d["bias"],
+                                   grad_weight=gw_buf, grad_bias=gb_buf, **_opts(c))
+    torch.cuda.synchronize()
+    assert gw.data_ptr() == gw_buf.data_ptr() and gb.data_ptr() == gb_buf.data_ptr()
+    assert_grad_close(t2np(gh), rgh, "grad_hidden")
+    assert_grad_close(t2np(gw) - gw0, rgw, "grad_weight (accumulated, minus prior)")
+    assert_grad_close(t2np(gb) - gb0, rgb, "grad_bias (accumulated, minus prior)")
+
+
 def test_all_rows_ignored_mean(flce_lib):
     import torch
     c = Case("all_ignored", 300, 64, 500, "bf16", 0.1, reduction="mean", weight_std=0.1)
