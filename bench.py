@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 import synth_inputs as si  # noqa: E402
 
-PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 (and fp16) MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "fwd+bwd tokens/s and TFLOP/s (8NHV) vs bf16 MFMA peak, N=8192 H=4096 V=128k"
@@ -140,7 +140,7 @@ def main():
     pf = flce.make_params(n, h, v, dtype=wl.dtype, grad_weight_dtype=wl.grad_weight_dtype, **opts)
     ws_f = torch.empty(flce.flce_workspace_size(pf, flce.FLCE_PASS_FORWARD), dtype=torch.uint8, device="cuda")
     ws_b = torch.empty(flce.flce_workspace_size(pf, flce.FLCE_PASS_BACKWARD), dtype=torch.uint8, device="cuda")
-    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
     loss = torch.empty(n if wl.reduction == "none" else 1, dtype=torch.float32, device="cuda")
     lse = torch.empty(n, dtype=torch.float32, device="cuda")
     nc = torch.empty(1, dtype=torch.int64, device="cuda")
@@ -195,7 +195,7 @@ def main():
     tflops = flop / (step_ms * 1e-3) / 1e12
     fwd_tflops = 2.0 * n * h * v / (fwd_ms * 1e-3) / 1e12
     bwd_tflops = 6.0 * n * h * v / (bwd_ms * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    peak = PEAK_BF16_TFLOPS if wl.dtype in ("bf16", "f16") else PEAK_F32_TFLOPS
     out = {
         "metric": METRIC,
         "value": n / (step_ms * 1e-3),

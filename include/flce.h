@@ -20,7 +20,10 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers, row-major and contiguous, 16-byte
  *    aligned.  hidden is (N, H), weight (V, H), bias (V) or NULL, targets (N)
- *    int64.  Floating inputs are all of params->dtype.
+ *    int64, or int32 with FLCE_TARGETS_INT32.  Floating inputs are all of
+ *    params->dtype: fp32, bf16 or fp16 (fused-linear-ce README, "Usage": the
+ *    signature's hidden/weight dtypes; quack's linear_cross_entropy_func takes
+ *    int or long targets).
  *  - The caller owns every buffer, including the workspace, which it sizes with
  *    flce_workspace_size.  The library allocates no device memory and keeps no
  *    mutable global state; calls on different streams with different
@@ -56,7 +59,7 @@ typedef enum {
   FLCE_ERR_TARGET_OUT_OF_RANGE = -5   /* reported by flce_get_status only                    */
 } flce_status;
 
-typedef enum { FLCE_F32 = 0, FLCE_BF16 = 1 } flce_dtype;
+typedef enum { FLCE_F32 = 0, FLCE_BF16 = 1, FLCE_F16 = 2 } flce_dtype;
 
 typedef enum {
   FLCE_REDUCTION_NONE = 0,
@@ -66,15 +69,18 @@ typedef enum {
 
 typedef enum { FLCE_PASS_FORWARD = 0, FLCE_PASS_BACKWARD = 1 } flce_pass;
 
-/* flce_params.flags: the backward pass adds its result to what the output
- * buffer already holds instead of overwriting it, e.g. to accumulate the
- * weight gradient over micro-batches without a separate add ("Chunked Linear
- * Loss" page, "Weight-gradient accumulation dtype": accumulate in the weight
- * dtype, or in fp32 with grad_weight_dtype = FLCE_F32).  The sum is formed in
- * fp32 and rounded once to the buffer's dtype. */
+/* flce_params.flags.
+ * FLCE_ACCUMULATE_GRAD_WEIGHT / _BIAS (backward): add the result to what the
+ * output buffer already holds instead of overwriting it, e.g. to accumulate
+ * the weight gradient over micro-batches without a separate add ("Chunked
+ * Linear Loss" page, "Weight-gradient accumulation dtype": accumulate in the
+ * weight dtype, or in fp32 with grad_weight_dtype = FLCE_F32).  The sum is
+ * formed in fp32 and rounded once to the buffer's dtype.
+ * FLCE_TARGETS_INT32 (both passes): `targets` points to int32 values. */
 typedef enum {
   FLCE_ACCUMULATE_GRAD_WEIGHT = 1,
-  FLCE_ACCUMULATE_GRAD_BIAS = 2
+  FLCE_ACCUMULATE_GRAD_BIAS = 2,
+  FLCE_TARGETS_INT32 = 4
 } flce_flags;
 
 typedef struct {
@@ -85,7 +91,7 @@ typedef struct {
   int32_t dtype;              /* flce_dtype of hidden, weight and bias                   */
   int32_t grad_weight_dtype;  /* flce_dtype of grad_weight; accumulated in fp32 always   */
   int32_t reduction;          /* flce_reduction                                          */
-  int32_t flags;              /* flce_flags bits (backward only); 0 = overwrite outputs  */
+  int32_t flags;              /* flce_flags bits; 0 = int64 targets, overwrite outputs   */
   float logit_scale;          /* multiplies (x.W^T + b); 1.0 = off                       */
   float softcap;              /* cap of cap*tanh(v/cap); <= 0 = off                      */
   float z_loss;               /* z-loss multiplier lambda >= 0; 0 = off                  */
@@ -111,7 +117,7 @@ int flce_workspace_size(const flce_params* p, int pass, size_t* bytes);
  * status word (see flce_get_status).
  */
 int flce_forward(const flce_params* p, const void* hidden, const void* weight, const void* bias,
-                 const int64_t* targets, float* loss, float* lse, int64_t* num_correct,
+                 const void* targets, float* loss, float* lse, int64_t* num_correct,
                  float* entropy_sum, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -123,9 +129,13 @@ int flce_forward(const flce_params* p, const void* hidden, const void* weight, c
  *  grad_weight: device (V, H) in params->grad_weight_dtype, accumulated in fp32.  Required.
  *  grad_bias:   device (V) in params->dtype, or NULL; must be NULL when bias is NULL.
  * Rows whose target is ignored (or out of range) get zero gradient.
+ * The logit gradient feeding the two contractions is held in the input dtype;
+ * for fp16 it is scaled by a power of two chosen per call (so that the small
+ * probabilities of a large vocabulary stay in fp16's normal range) and the
+ * factor is divided out exactly in fp32.
  */
 int flce_backward(const flce_params* p, const void* hidden, const void* weight, const void* bias,
-                  const int64_t* targets, const float* lse, const float* grad_loss,
+                  const void* targets, const float* lse, const float* grad_loss,
                   void* grad_hidden, void* grad_weight, void* grad_bias, void* workspace,
                   size_t workspace_bytes, void* stream);
 

@@ -30,11 +30,14 @@ FLCE_ERR_TARGET_OUT_OF_RANGE = -5
 
 FLCE_F32 = 0
 FLCE_BF16 = 1
+FLCE_F16 = 2
+DTYPES = {"f32": FLCE_F32, "bf16": FLCE_BF16, "f16": FLCE_F16}
 REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 FLCE_PASS_FORWARD = 0
 FLCE_PASS_BACKWARD = 1
 FLCE_ACCUMULATE_GRAD_WEIGHT = 1
 FLCE_ACCUMULATE_GRAD_BIAS = 2
+FLCE_TARGETS_INT32 = 4
 
 EXPORTED = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_get_status",
             "flce_status_string", "flce_version")
@@ -142,10 +145,10 @@ def make_params(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
                 grad_weight_dtype: Optional[str] = None, logit_scale: float = 1.0,
                 softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
                 reduction: str = "mean", accumulate_grad_weight: bool = False,
-                accumulate_grad_bias: bool = False) -> flce_params:
+                accumulate_grad_bias: bool = False, targets_int32: bool = False) -> flce_params:
     if reduction not in REDUCTIONS:
         raise ValueError(f"invalid reduction {reduction!r}")
-    dt = {"bf16": FLCE_BF16, "f32": FLCE_F32}
+    dt = DTYPES
     p = flce_params()
     p.n_tokens, p.hidden, p.vocab, p.ignore_index = n_tokens, hidden, vocab, ignore_index
     p.dtype = dt[dtype]
@@ -155,7 +158,8 @@ def make_params(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
     p.softcap = softcap if softcap else 0.0
     p.z_loss = z_loss
     p.flags = (FLCE_ACCUMULATE_GRAD_WEIGHT if accumulate_grad_weight else 0) | \
-              (FLCE_ACCUMULATE_GRAD_BIAS if accumulate_grad_bias else 0)
+              (FLCE_ACCUMULATE_GRAD_BIAS if accumulate_grad_bias else 0) | \
+              (FLCE_TARGETS_INT32 if targets_int32 else 0)
     return p
 
 
@@ -172,9 +176,20 @@ def _dtype_name(t) -> str:
     import torch
     if t.dtype == torch.bfloat16:
         return "bf16"
+    if t.dtype == torch.float16:
+        return "f16"
     if t.dtype == torch.float32:
         return "f32"
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _targets_int32(t) -> bool:
+    import torch
+    if t.dtype == torch.int64:
+        return False
+    if t.dtype == torch.int32:
+        return True
+    raise TypeError(f"targets must be int64 or int32, not {t.dtype}")
 
 
 def _check(t, name):
@@ -192,7 +207,8 @@ def forward(hidden, weight, targets, bias=None, *, logit_scale: float = 1.0,
     n, h = hidden.shape
     v = weight.shape[0]
     p = make_params(n, h, v, dtype=_dtype_name(hidden), logit_scale=logit_scale, softcap=softcap,
-                    z_loss=z_loss, ignore_index=ignore_index, reduction=reduction)
+                    z_loss=z_loss, ignore_index=ignore_index, reduction=reduction,
+                    targets_int32=_targets_int32(targets))
     dev = hidden.device
     ws_bytes = flce_workspace_size(p, FLCE_PASS_FORWARD)
     if workspace is None or workspace.numel() < ws_bytes:
@@ -234,12 +250,13 @@ def backward(hidden, weight, targets, lse, grad_loss, bias=None, *, logit_scale:
         raise ValueError("grad_bias must match bias")
     p = make_params(n, h, v, dtype=dt, grad_weight_dtype=grad_weight_dtype, logit_scale=logit_scale,
                     softcap=softcap, z_loss=z_loss, ignore_index=ignore_index, reduction=reduction,
-                    accumulate_grad_weight=grad_weight is not None, accumulate_grad_bias=grad_bias is not None)
+                    accumulate_grad_weight=grad_weight is not None, accumulate_grad_bias=grad_bias is not None,
+                    targets_int32=_targets_int32(targets))
     dev = hidden.device
     ws_bytes = flce_workspace_size(p, FLCE_PASS_BACKWARD)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
     gh = torch.empty((n, h), dtype=hidden.dtype, device=dev)
     gw = grad_weight if grad_weight is not None else torch.empty((v, h), dtype=tdt[grad_weight_dtype or dt], device=dev)
     gb = grad_bias if grad_bias is not None else (torch.empty(v, dtype=bias.dtype, device=dev) if bias is not None else None)

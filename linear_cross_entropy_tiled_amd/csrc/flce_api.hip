@@ -22,17 +22,19 @@ static constexpr int64_t kTargetWorkgroups = 256;
 int make_plan(const flce_params* p, Plan* pl) {
   if (!p || !pl) return FLCE_ERR_INVALID_ARG;
   if (p->n_tokens < 0 || p->hidden <= 0 || p->vocab <= 0) return FLCE_ERR_INVALID_ARG;
-  if (p->dtype != FLCE_F32 && p->dtype != FLCE_BF16) return FLCE_ERR_INVALID_ARG;
-  if (p->grad_weight_dtype != FLCE_F32 && p->grad_weight_dtype != FLCE_BF16) return FLCE_ERR_INVALID_ARG;
+  if (p->dtype != FLCE_F32 && p->dtype != FLCE_BF16 && p->dtype != FLCE_F16) return FLCE_ERR_INVALID_ARG;
+  if (p->grad_weight_dtype != FLCE_F32 && p->grad_weight_dtype != FLCE_BF16 && p->grad_weight_dtype != FLCE_F16)
+    return FLCE_ERR_INVALID_ARG;
   if (p->reduction != FLCE_REDUCTION_NONE && p->reduction != FLCE_REDUCTION_SUM &&
       p->reduction != FLCE_REDUCTION_MEAN)
     return FLCE_ERR_INVALID_ARG;
-  if ((p->flags & ~(FLCE_ACCUMULATE_GRAD_WEIGHT | FLCE_ACCUMULATE_GRAD_BIAS)) != 0 || p->reserved_f != 0.0f)
+  if ((p->flags & ~(FLCE_ACCUMULATE_GRAD_WEIGHT | FLCE_ACCUMULATE_GRAD_BIAS | FLCE_TARGETS_INT32)) != 0 ||
+      p->reserved_f != 0.0f)
     return FLCE_ERR_INVALID_ARG;
   if (!isfinite(p->logit_scale) || !isfinite(p->softcap) || !isfinite(p->z_loss) || p->z_loss < 0.0f)
     return FLCE_ERR_INVALID_ARG;
   if (p->hidden % 8 != 0) return FLCE_ERR_UNSUPPORTED;
-  const int esize = p->dtype == FLCE_BF16 ? 2 : 4;
+  const int esize = p->dtype == FLCE_F32 ? 4 : 2;
   // 32-bit buffer offsets and int indices inside the kernels
   if (p->n_tokens > (int64_t(1) << 30) || p->vocab > (int64_t(1) << 30) || p->hidden > (int64_t(1) << 20))
     return FLCE_ERR_UNSUPPORTED;
@@ -49,6 +51,7 @@ int make_plan(const flce_params* p, Plan* pl) {
   P.reduction = p->reduction;
   P.accum_gw = (p->flags & FLCE_ACCUMULATE_GRAD_WEIGHT) != 0;
   P.accum_gb = (p->flags & FLCE_ACCUMULATE_GRAD_BIAS) != 0;
+  P.tgt_i32 = (p->flags & FLCE_TARGETS_INT32) != 0;
   P.scale = p->logit_scale;
   P.cap = p->softcap > 0.0f ? p->softcap : 0.0f;
   P.z_loss = p->z_loss;
@@ -111,7 +114,7 @@ int make_plan(const flce_params* p, Plan* pl) {
   P.b_xt = o;
   o = align_up(o + size_t(P.N_pad) * P.H * esize, 256);
   P.b_ghacc = o;
-  if (P.dtype == FLCE_BF16 && P.n_chunks > 1) o = align_up(o + size_t(P.N) * P.H * 4, 256);
+  if (P.dtype != FLCE_F32 && P.n_chunks > 1) o = align_up(o + size_t(P.N) * P.H * 4, 256);
   P.b_ghpart = o;
   if (P.gh_parts > 1) o = align_up(o + size_t(P.gh_parts) * P.N * P.H * 4, 256);
   P.b_gbpart = o;
@@ -154,7 +157,7 @@ int flce_workspace_size(const flce_params* p, int pass, size_t* bytes) {
 }
 
 int flce_forward(const flce_params* p, const void* hidden, const void* weight, const void* bias,
-                 const int64_t* targets, float* loss, float* lse, int64_t* num_correct,
+                 const void* targets, float* loss, float* lse, int64_t* num_correct,
                  float* entropy_sum, void* workspace, size_t workspace_bytes, void* stream) {
   Plan pl;
   int rc = make_plan(p, &pl);
@@ -174,7 +177,7 @@ int flce_forward(const flce_params* p, const void* hidden, const void* weight, c
 }
 
 int flce_backward(const flce_params* p, const void* hidden, const void* weight, const void* bias,
-                  const int64_t* targets, const float* lse, const float* grad_loss, void* grad_hidden,
+                  const void* targets, const float* lse, const float* grad_loss, void* grad_hidden,
                   void* grad_weight, void* grad_bias, void* workspace, size_t workspace_bytes,
                   void* stream) {
   Plan pl;

@@ -7,12 +7,20 @@
 // in fp32 and cast once ("Chunked Linear Loss", "Weight-gradient accumulation
 // dtype").  Per vocabulary chunk of width Vc:
 //   dlogits  D[t][v] = scale * softcap'(z) * c_t * ((1 + 2 lam LSE_t) p_tv - [v = t_t])
-//            into a scratch of N x Vc (bf16 for bf16 inputs), plus per
+//            into a scratch of N x Vc in the input dtype, plus per
 //            token-tile column sums of D for grad_bias;
 //   gw       grad_weight[v][:] = sum_t D[t][v] hidden[t][:]    (written once per row);
 //   gh       grad_hidden[t][:] += sum_v D[t][v] weight[v][:]   (fp32, fixed chunk order).
 // No float atomics: every output element has exactly one writer per launch,
 // so results are bitwise reproducible.
+//
+// fp16 dlogits: with "mean" over thousands of tokens most entries of D are
+// far below fp16's smallest normal (p ~ 1/V times c ~ 1/n_valid), so D is
+// stored multiplied by a power of two 2^s chosen per call from the largest
+// possible |D| (|scale| max_t (|coefA_t| + |coefB_t|)) to put that bound just
+// under 2^14.  The contractions accumulate in fp32 and their epilogues
+// multiply by 2^-s, which is exact, so the results are those of an unscaled
+// D with fp16's full precision.  For bf16 and fp32 the factor is 1.
 #include "flce_device.h"
 #include "flce_internal.h"
 
@@ -23,7 +31,8 @@ namespace flce {
 // needs.  One block; N is at most a few hundred thousand rows.
 // ---------------------------------------------------------------------------
 struct PrepArgs {
-  const int64_t* targets;
+  const void* targets;
+  int tgt_i32;
   const float* lse;
   const float* grad_loss;
   int N, V, N_pad, reduction;
@@ -34,14 +43,18 @@ struct PrepArgs {
   float* lseL;    // LSE_i * log2(e)
   int* tgt;       // target or -1
   int* status;
+  float* dscale;  // [0] = 2^s, [1] = 2^-s (see above)
+  int f16_d;      // dlogits are fp16: choose s; else s = 0
+  float abs_scale;
 };
 
 __global__ __launch_bounds__(1024) void bwd_prep_kernel(PrepArgs a) {
   __shared__ int sv[1024], sb[1024];
+  __shared__ float sm[1024];
   const int tid = threadIdx.x;
   int nv = 0, bad = 0;
   for (int i = tid; i < a.N; i += 1024) {
-    const int64_t t = a.targets[i];
+    const int64_t t = load_target(a.targets, i, a.tgt_i32);
     const bool in_range = t >= 0 && t < a.V;
     nv += (t != a.ignore_index && in_range) ? 1 : 0;
     bad |= (t != a.ignore_index && !in_range) ? 1 : 0;
@@ -59,11 +72,12 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(PrepArgs a) {
   const int n_valid = sv[0];
   const float g0 = a.reduction == FLCE_REDUCTION_NONE ? 0.0f : a.grad_loss[0];
   const float c_all = a.reduction == FLCE_REDUCTION_SUM ? g0 : (n_valid > 0 ? g0 / (float)n_valid : 0.0f);
+  float dmax = 0.0f;
   for (int i = tid; i < a.N_pad; i += 1024) {
     float ca = 0.0f, cb = 0.0f, ll = 0.0f;
     int tg = -1;
     if (i < a.N) {
-      const int64_t t = a.targets[i];
+      const int64_t t = load_target(a.targets, i, a.tgt_i32);
       const bool valid = t != a.ignore_index && t >= 0 && t < a.V;
       const float lse = a.lse[i];
       ll = lse * kLog2e;
@@ -78,12 +92,33 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(PrepArgs a) {
     a.coefB[i] = cb;
     a.lseL[i] = ll;
     a.tgt[i] = tg;
+    dmax = fmaxf(dmax, fabsf(ca) + fabsf(cb));
   }
-  if (tid == 0) a.status[0] = sb[0] ? FLCE_ERR_TARGET_OUT_OF_RANGE : FLCE_OK;
+  if (a.f16_d) {
+    sm[tid] = dmax;
+    __syncthreads();
+    for (int w = 512; w > 0; w >>= 1) {
+      if (tid < w) sm[tid] = fmaxf(sm[tid], sm[tid + w]);
+      __syncthreads();
+    }
+  }
+  if (tid == 0) {
+    a.status[0] = sb[0] ? FLCE_ERR_TARGET_OUT_OF_RANGE : FLCE_OK;
+    int s = 0;
+    const float bound = a.f16_d ? sm[0] * a.abs_scale : 0.0f;   // >= every |D|
+    if (bound > 0.0f && isfinite(bound)) {
+      int e;
+      frexpf(bound, &e);   // bound < 2^e
+      s = min(max(14 - e, -120), 120);
+    }
+    a.dscale[0] = ldexpf(1.0f, s);
+    a.dscale[1] = ldexpf(1.0f, -s);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Stores of 4 consecutive values (one lane, 4 consecutive rows of a tile).
+// Stores of 4 consecutive values (one lane, 4 consecutive rows of a tile),
+// rounded to nearest even.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
   bf16x4 v;
@@ -92,6 +127,14 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
   v[2] = (bf16)c;
   v[3] = (bf16)d;
   *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(f16* p, float a, float b, float c, float d) {
+  f16x4 v;
+  v[0] = (f16)a;
+  v[1] = (f16)b;
+  v[2] = (f16)c;
+  v[3] = (f16)d;
+  *reinterpret_cast<f16x4*>(p) = v;
 }
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   f32x4 v;
@@ -114,6 +157,27 @@ template <> __device__ __forceinline__ void load4<bf16>(const bf16* p, float* ou
 #pragma unroll
   for (int j = 0; j < 4; j++) out[j] = (float)v[j];
 }
+template <> __device__ __forceinline__ void load4<f16>(const f16* p, float* out) {
+  const f16x4 v = *reinterpret_cast<const f16x4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; j++) out[j] = (float)v[j];
+}
+
+// grad_weight element types (FLCE_F32, FLCE_BF16, FLCE_F16): 4 consecutive
+// values added to (when accumulating) and stored in the buffer's type.
+__device__ __forceinline__ void update4(void* base, size_t o, int type, bool accumulate, float* c) {
+  if (accumulate) {
+    float prev[4];
+    if (type == FLCE_F32) load4<float>(reinterpret_cast<const float*>(base) + o, prev);
+    else if (type == FLCE_BF16) load4<bf16>(reinterpret_cast<const bf16*>(base) + o, prev);
+    else load4<f16>(reinterpret_cast<const f16*>(base) + o, prev);
+#pragma unroll
+    for (int j = 0; j < 4; j++) c[j] += prev[j];
+  }
+  if (type == FLCE_F32) store4(reinterpret_cast<float*>(base) + o, c[0], c[1], c[2], c[3]);
+  else if (type == FLCE_BF16) store4(reinterpret_cast<bf16*>(base) + o, c[0], c[1], c[2], c[3]);
+  else store4(reinterpret_cast<f16*>(base) + o, c[0], c[1], c[2], c[3]);
+}
 
 // ---------------------------------------------------------------------------
 // dlogits: one 256 (vocab) x 256 (token) tile per workgroup.
@@ -135,6 +199,7 @@ struct DlogitsArgs {
   int ldD;
   float* gb_part;   // [n_tt][ld_gb]
   int ld_gb;
+  const float* dscale;   // [0]: factor D is stored with
 };
 
 template <typename T, bool HAS_BIAS, bool SOFTCAP>
@@ -184,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
   tile_mainloop<T, true, true>(da, db, KT, grouped_share(vt, tt), acc);
 
   // ---- epilogue, one 32-row MFMA tile at a time:
-  //   D = scale * softcap'(z) * (coefA * p - [row = target] * coefB),
+  //   D = 2^s * scale * softcap'(z) * (coefA * p - [row = target] * coefB),
   // stored as 4 consecutive vocabulary rows per lane, plus the column sums
   // over this tile's 256 tokens for grad_bias
   const int vw = v0 + wm * kWaveM;
@@ -196,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
   // exponent's constant term (or -LSE log2e without the cap).
   const float s2 = SOFTCAP ? a.scale * a.two_log2e_over_cap : a.scale;   // scale folded into the exp argument
   const float k1 = -a.two_cap * kLog2e;
-  const float cmul = SOFTCAP ? 4.0f * a.scale : a.scale;
+  const float cmul = (SOFTCAP ? 4.0f * a.scale : a.scale) * a.dscale[0];
   float cAs[kNI], cBs[kNI], k0[kNI];
   int rel[kNI];
 #pragma unroll
@@ -308,8 +373,9 @@ struct GwArgs {
   int cv0;
   int n_ht, n_vt_c;
   void* gw;
-  int gw_f32;
+  int gw_type;      // flce_dtype of grad_weight
   int accumulate;   // add to grad_weight's current contents
+  const float* dscale;   // [1]: 2^-s, undoes the factor D is stored with
 };
 
 template <typename T>
@@ -342,6 +408,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gw_kernel(GwArgs a) {
   zero_acc(acc);
   tile_mainloop<T, true, false>(da, db, KT, grouped_share(ht, vt), acc);
 
+  const float inv = a.dscale[1];
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
     const int v = a.cv0 + vl0 + wn * kWaveN + ni * 32 + (lane & 31);
@@ -353,18 +420,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gw_kernel(GwArgs a) {
         const int h = h0 + wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5);
         if (h >= a.H) continue;
         const size_t o = (size_t)v * a.H + h;
-        float c[4] = {acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]};
-        if (a.accumulate) {
-          float prev[4];
-          if (a.gw_f32) load4<float>(reinterpret_cast<const float*>(a.gw) + o, prev);
-          else load4<bf16>(reinterpret_cast<const bf16*>(a.gw) + o, prev);
-#pragma unroll
-          for (int j = 0; j < 4; j++) c[j] += prev[j];
-        }
-        if (a.gw_f32)
-          store4(reinterpret_cast<float*>(a.gw) + o, c[0], c[1], c[2], c[3]);
-        else
-          store4(reinterpret_cast<bf16*>(a.gw) + o, c[0], c[1], c[2], c[3]);
+        float c[4] = {acc[mi][ni][4 * g] * inv, acc[mi][ni][4 * g + 1] * inv, acc[mi][ni][4 * g + 2] * inv,
+                      acc[mi][ni][4 * g + 3] * inv};
+        update4(a.gw, o, a.gw_type, a.accumulate != 0, c);
       }
   }
 }
@@ -391,6 +449,7 @@ struct GhArgs {
   int parts;        // > 1: K split; split p covers stages [p kt_per_part, (p+1) kt_per_part)
   int kt_per_part;
   float* part;      // parts x N x H fp32 partials (parts > 1)
+  const float* dscale;   // [1]: 2^-s, undoes the factor D is stored with
 };
 
 template <typename T>
@@ -433,6 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gh_kernel(GhArgs a) {
   zero_acc(acc);
   tile_mainloop<T, false, true>(da, db, KT, grouped_share(ht, tt), acc);
 
+  const float inv = a.dscale[1];
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
     const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
@@ -444,8 +504,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gh_kernel(GhArgs a) {
         const int h = h0 + wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5);
         if (h >= a.H) continue;
         const size_t o = (size_t)t * a.H + h;
-        float c0 = acc[mi][ni][4 * g], c1 = acc[mi][ni][4 * g + 1];
-        float c2 = acc[mi][ni][4 * g + 2], c3 = acc[mi][ni][4 * g + 3];
+        float c0 = acc[mi][ni][4 * g] * inv, c1 = acc[mi][ni][4 * g + 1] * inv;
+        float c2 = acc[mi][ni][4 * g + 2] * inv, c3 = acc[mi][ni][4 * g + 3] * inv;
         if (a.parts > 1) {   // partial of this split; bwd_gh_reduce applies the mode
           store4(a.part + (size_t)split * a.N * a.H + o, c0, c1, c2, c3);
           continue;
@@ -461,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gh_kernel(GhArgs a) {
           float* dst = (a.mode <= 1) ? a.accb + o : reinterpret_cast<float*>(a.out) + o;
           store4(dst, c0, c1, c2, c3);
         } else {
-          store4(reinterpret_cast<bf16*>(a.out) + o, c0, c1, c2, c3);
+          store4(reinterpret_cast<T*>(a.out) + o, c0, c1, c2, c3);
         }
       }
   }
@@ -503,21 +563,23 @@ __global__ __launch_bounds__(256) void transpose_hidden_kernel(const T* x, int N
   }
 }
 
-// grad_bias[v] = sum over token tiles of the per-tile column sums, in order.
+// grad_bias[v] = sum over token tiles of the per-tile column sums, in order
+// (sums of the stored D, so times 2^-s).
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_gb_reduce(const float* part, int n_tt, int ld, int V, T* gb,
-                                                     int accumulate) {
+                                                     int accumulate, const float* dscale) {
   const int v = blockIdx.x * 256 + threadIdx.x;
   if (v >= V) return;
   float s = 0.0f;
   for (int i = 0; i < n_tt; i++) s += part[(size_t)i * ld + v];
+  s *= dscale[1];
   if (accumulate) s += load_elem<T>(gb, v);
   gb[v] = (T)s;
 }
 
 template <typename T>
 static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const void* weight,
-                                    const void* bias, const int64_t* targets, const float* lse,
+                                    const void* bias, const void* targets, const float* lse,
                                     const float* grad_loss, void* grad_hidden, void* grad_weight,
                                     void* grad_bias, char* ws, hipStream_t st) {
   float* coefA = reinterpret_cast<float*>(ws + pl.b_coefA);
@@ -529,6 +591,7 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
 
   PrepArgs pa;
   pa.targets = targets;
+  pa.tgt_i32 = pl.tgt_i32 ? 1 : 0;
   pa.lse = lse;
   pa.grad_loss = grad_loss;
   pa.N = (int)pl.N;
@@ -542,6 +605,10 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
   pa.lseL = lseL;
   pa.tgt = tgt;
   pa.status = reinterpret_cast<int*>(ws);
+  float* dscale = reinterpret_cast<float*>(ws + kDscaleOffset);
+  pa.dscale = dscale;
+  pa.f16_d = pl.dtype == FLCE_F16;
+  pa.abs_scale = fabsf(pl.scale);
   bwd_prep_kernel<<<1, 1024, 0, st>>>(pa);
 
   T* hiddenT = reinterpret_cast<T*>(ws + pl.b_xt);
@@ -581,6 +648,7 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       d.ldD = ldD;
       d.gb_part = gb_part;
       d.ld_gb = (int)pl.V_pad;
+      d.dscale = dscale;
       const int nwg = n_vt_c * (int)pl.n_tt;
       if (pl.has_bias) {
         if (pl.cap > 0) bwd_dlogits_kernel<T, true, true><<<nwg, kThreads, 0, st>>>(d);
@@ -603,7 +671,8 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       g.n_ht = (int)pl.n_ht;
       g.n_vt_c = n_vt_c;
       g.gw = grad_weight;
-      g.gw_f32 = pl.gw_dtype == FLCE_F32;
+      g.gw_type = pl.gw_dtype;
+      g.dscale = dscale;
       g.accumulate = pl.accum_gw ? 1 : 0;
       bwd_gw_kernel<T><<<(int)pl.n_ht * n_vt_c, kThreads, 0, st>>>(g);
     }
@@ -626,6 +695,7 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       h.parts = pl.gh_parts;
       h.kt_per_part = pl.gh_kt_per_part;
       h.part = reinterpret_cast<float*>(ws + pl.b_ghpart);
+      h.dscale = dscale;
       bwd_gh_kernel<T><<<(int)(pl.n_ht * pl.n_tt) * pl.gh_parts, kThreads, 0, st>>>(h);
       if (pl.gh_parts > 1) {
         const int64_t n4 = pl.N * pl.H / 4;
@@ -637,18 +707,21 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
   if (grad_bias) {
     bwd_gb_reduce<T><<<(int)((pl.V + 255) / 256), 256, 0, st>>>(gb_part, (int)pl.n_tt, (int)pl.V_pad,
                                                                (int)pl.V, reinterpret_cast<T*>(grad_bias),
-                                                               pl.accum_gb ? 1 : 0);
+                                                               pl.accum_gb ? 1 : 0, dscale);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_backward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
-                           const int64_t* targets, const float* lse, const float* grad_loss,
+                           const void* targets, const float* lse, const float* grad_loss,
                            void* grad_hidden, void* grad_weight, void* grad_bias, char* ws,
                            hipStream_t st) {
   if (pl.dtype == FLCE_BF16)
     return launch_backward_t<bf16>(pl, hidden, weight, bias, targets, lse, grad_loss, grad_hidden,
                                    grad_weight, grad_bias, ws, st);
+  if (pl.dtype == FLCE_F16)
+    return launch_backward_t<f16>(pl, hidden, weight, bias, targets, lse, grad_loss, grad_hidden,
+                                  grad_weight, grad_bias, ws, st);
   return launch_backward_t<float>(pl, hidden, weight, bias, targets, lse, grad_loss, grad_hidden,
                                   grad_weight, grad_bias, ws, st);
 }

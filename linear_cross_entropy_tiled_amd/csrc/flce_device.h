@@ -5,7 +5,7 @@
 // Tile main loop: C[256 x 256] += A[256 x K] . B[256 x K]^T with fp32
 // accumulation, 8 waves (2 along M x 4 along N, two per SIMD), each wave
 // owning a 128 x 64 block as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16
-// (v_mfma_f32_32x32x2_f32 for fp32 inputs).  Two waves per SIMD keep enough
+// (v_mfma_f32_32x32x16_f16 for fp16, v_mfma_f32_32x32x2_f32 for fp32 inputs).  Two waves per SIMD keep enough
 // LDS reads in flight to feed the matrix cores; with one wave per SIMD
 // (4 x 128 x 128) the same loop measured 6-10% slower.
 //
@@ -20,7 +20,7 @@
 // about a quarter of the bytes per clock of ds_read_b128, so a contraction
 // uses at most one MNMAJOR operand.
 //
-// K order: a stage is 128 bytes of K per row (64 bf16 / 32 fp32), eight
+// K order: a stage is 128 bytes of K per row (64 bf16 or fp16 / 32 fp32), eight
 // 16-byte chunks.  In sub-step s (0..3) lane half h (lane / 32) contracts
 // chunk 4h + s.  Any order is correct as long as both operands use the same
 // one.
@@ -34,6 +34,9 @@ namespace flce {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -51,7 +54,7 @@ constexpr float kMasked = -0x1p100f;
 
 constexpr int kBM = 256;            // tile rows (A operand)
 constexpr int kBN = 256;            // tile cols (B operand)
-constexpr int kBKB = 128;           // bytes of K per pipeline stage per row (64 bf16 / 32 fp32)
+constexpr int kBKB = 128;           // bytes of K per pipeline stage per row (64 16-bit / 32 fp32)
 constexpr int kWavesM = 2, kWavesN = 4;
 constexpr int kWaves = kWavesM * kWavesN;        // 8 waves
 constexpr int kThreads = 64 * kWaves;            // 512 threads
@@ -160,6 +163,11 @@ template <> __device__ __forceinline__ void lds_vec4<bf16>(const char* v, int i,
 #pragma unroll
   for (int j = 0; j < 4; j++) out[j] = (float)x[j];
 }
+template <> __device__ __forceinline__ void lds_vec4<f16>(const char* v, int i, float* out) {
+  const f16x4 x = *reinterpret_cast<const f16x4*>(v + 2 * i);
+#pragma unroll
+  for (int j = 0; j < 4; j++) out[j] = (float)x[j];
+}
 
 template <typename T, bool KMAJOR>
 struct OperandLoader {
@@ -203,7 +211,7 @@ struct OperandLoader {
   }
 
   // L2 prefetch of 128-byte line j (0..255) of stage kt: K-major row j;
-  // M/N-major bf16 row 64 kt + j/4, column block j%4.  Inactive lanes fetch
+  // M/N-major 16-bit row 64 kt + j/4, column block j%4.  Inactive lanes fetch
   // nothing.
   __device__ __forceinline__ void prefetch_line(int kt, int j, bool active, uint32_t sink) const {
     uint32_t voff;
@@ -255,22 +263,25 @@ template <typename T, bool KMAJOR> struct Frag;
 // kc ^ ((r >> 1) & 7).  A ds_read_b128 is served 16 lanes (16 consecutive
 // rows, two per 256-byte bank line) at a time, and this spreads them over all
 // 64 banks.
-template <> struct Frag<bf16, true> {
-  typedef bf16x8 type;
+// (The same reads serve both 16-bit types; only the register type differs.)
+template <typename V8> struct Frag16K {
+  typedef V8 type;
   __device__ __forceinline__ static type read(const char* op, int c0, int s, int lane) {
     const int row = c0 + (lane & 31);
     const int kc = 4 * (lane >> 5) + s;
     const int off = row * kBKB + ((kc ^ ((row >> 1) & 7)) << 4);
-    return *reinterpret_cast<const bf16x8*>(op + off);
+    return *reinterpret_cast<const V8*>(op + off);
   }
 };
+template <> struct Frag<bf16, true> : Frag16K<bf16x8> {};
+template <> struct Frag<f16, true> : Frag16K<f16x8> {};
 
-// MNMAJOR bf16 rows are 512 B (256 elements); 8-byte unit u of row r sits at
+// MNMAJOR 16-bit rows are 512 B (256 elements); 8-byte unit u of row r sits at
 // unit u ^ ((r & 3) << 3).  The transposing read gives lane i of each 16-lane
 // group element (4 j' + i/4, i%4) of the 16 chunks its group addressed, so the
 // group addresses rows k..k+3 at columns c, c+4, c+8, c+12.
-template <> struct Frag<bf16, false> {
-  typedef bf16x8 type;
+template <typename V8> struct Frag16MN {
+  typedef V8 type;
   __device__ __forceinline__ static type read(const char* op, int c0, int s, int lane) {
     const int g = lane >> 4, kk = lane & 15, j = kk >> 2, q = kk & 3;
     const int row = 32 * (g >> 1) + 8 * s + j;
@@ -280,9 +291,11 @@ template <> struct Frag<bf16, false> {
     i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(op + off + 4 * 512));
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, v);
+    return __builtin_bit_cast(V8, v);
   }
 };
+template <> struct Frag<bf16, false> : Frag16MN<bf16x8> {};
+template <> struct Frag<f16, false> : Frag16MN<f16x8> {};
 
 // fp32: chunk kc holds K = 4 kc + j, j = 0..3 (one v_mfma_f32_32x32x2_f32 each).
 template <> struct Frag<float, true> {
@@ -309,6 +322,9 @@ template <> struct Frag<float, false> {
 
 __device__ __forceinline__ void mma(f32x16& c, const bf16x8& a, const bf16x8& b) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& c, const f16x8& a, const f16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ void mma(f32x16& c, const f32x4& a, const f32x4& b) {
 #pragma unroll
@@ -355,7 +371,7 @@ struct L2Share {
 constexpr int kPrefetchAhead = 2;
 static __shared__ __attribute__((aligned(256))) char g_prefetch_sink[256];
 
-// Issues this wave's share of the prefetch of stage kt (bf16 only); returns
+// Issues this wave's share of the prefetch of stage kt (16-bit types only); returns
 // whether the wave issued a load (wave-uniform).
 template <typename T, bool A_KMAJOR, bool B_KMAJOR>
 __device__ __forceinline__ bool prefetch_stage(const OperandLoader<T, A_KMAJOR>& la,
@@ -382,7 +398,7 @@ __device__ __forceinline__ bool prefetch_stage(const OperandLoader<T, A_KMAJOR>&
   }
 }
 
-// Instruction order inside one sub-step (bf16): the kMI x kNI = 8 MFMAs with
+// Instruction order inside one sub-step (16-bit types): the kMI x kNI = 8 MFMAs with
 // the NR LDS reads of the next sub-step slotted between them, front-loaded so
 // the reads are back before they are needed.  Left to itself the compiler
 // clusters the reads right before their first use and then waits on them.
@@ -400,7 +416,7 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 }
 
 // LDS read instructions per sub-step: one per K-major fragment, two
-// (transposing 8-byte reads) per M/N-major bf16 fragment.
+// (transposing 8-byte reads) per M/N-major 16-bit fragment.
 template <bool A_KMAJOR, bool B_KMAJOR>
 constexpr int reads_per_substep() {
   return (A_KMAJOR ? kMI : 2 * kMI) + (B_KMAJOR ? kNI : 2 * kNI);
@@ -517,5 +533,11 @@ __device__ __forceinline__ L2Share grouped_share(int tm, int tn) {
 template <typename T> __device__ __forceinline__ float load_elem(const T* p, int64_t i);
 template <> __device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) { return p[i]; }
 template <> __device__ __forceinline__ float load_elem<bf16>(const bf16* p, int64_t i) { return (float)p[i]; }
+template <> __device__ __forceinline__ float load_elem<f16>(const f16* p, int64_t i) { return (float)p[i]; }
+
+// Target i of an int64 or int32 target array.
+__device__ __forceinline__ int64_t load_target(const void* p, int64_t i, int int32) {
+  return int32 ? (int64_t) reinterpret_cast<const int32_t*>(p)[i] : reinterpret_cast<const int64_t*>(p)[i];
+}
 
 }  // namespace flce

@@ -14,7 +14,8 @@ struct FwdTileArgs {
   const char* hidden;
   const char* weight;
   const void* bias;
-  const int64_t* targets;
+  const void* targets;
+  int tgt_i32;
   int N, H, V;
   int64_t ignore_index;
   float scale, cap, two_log2e_over_cap, two_cap;
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
     const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
-    const int64_t tv = t < a.N ? a.targets[t] : a.ignore_index;
+    const int64_t tv = t < a.N ? load_target(a.targets, t, a.tgt_i32) : a.ignore_index;
     tgt[ni] = (tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1;
     st[ni].m = kMasked;
     st[ni].l = 0.0f;
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int v0 = vt * 256;
     const char* bias_tile = bias_lds[(vt - vt_begin) & 1];
-    // the range is rounded up to whole 4-byte words so that an odd last bf16
+    // the range is rounded up to whole 4-byte words so that an odd last 16-bit
     // entry still arrives: its word lies in the same page as the entry (the
     // bias is 16-byte aligned), and its other half only feeds masked rows
     if (HAS_BIAS && wave == 0)
@@ -269,7 +270,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
 // Finalize: merge the S splits of each row in order, then per-block sums.
 // ---------------------------------------------------------------------------
 struct FinArgs {
-  const int64_t* targets;
+  const void* targets;
+  int tgt_i32;
   int N, V, S, N_pad, reduction;
   int64_t ignore_index;
   float z_loss;
@@ -313,7 +315,7 @@ __global__ __launch_bounds__(256) void fwd_finalize_rows(FinArgs a) {
     }
     const float lse = r.m + fast_log2(r.l) * kLn2;
     const float ent = lse - r.T / r.l;
-    const int64_t t = a.targets[i];
+    const int64_t t = load_target(a.targets, i, a.tgt_i32);
     const bool in_range = t >= 0 && t < a.V;
     const bool valid = t != a.ignore_index && in_range;
     bad = (t != a.ignore_index && !in_range) ? 1 : 0;
@@ -419,7 +421,7 @@ static void launch_fwd_tiles(const Plan& pl, const FwdTileArgs& args, int nwg, h
 }
 
 hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
-                          const int64_t* targets, float* loss, float* lse, int64_t* num_correct,
+                          const void* targets, float* loss, float* lse, int64_t* num_correct,
                           float* entropy_sum, char* ws, hipStream_t st) {
   const size_t NP = (size_t)pl.N_pad * pl.S;
   float* part_m = reinterpret_cast<float*>(ws + pl.f_part);
@@ -435,6 +437,7 @@ hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight
     a.weight = static_cast<const char*>(weight);
     a.bias = bias;
     a.targets = targets;
+    a.tgt_i32 = pl.tgt_i32 ? 1 : 0;
     a.N = (int)pl.N;
     a.H = (int)pl.H;
     a.V = (int)pl.V;
@@ -453,11 +456,13 @@ hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight
     a.part_zt = part_zt;
     const int nwg = (int)(pl.n_tt * pl.S);
     if (pl.dtype == FLCE_BF16) launch_fwd_tiles<bf16>(pl, a, nwg, st);
+    else if (pl.dtype == FLCE_F16) launch_fwd_tiles<f16>(pl, a, nwg, st);
     else launch_fwd_tiles<float>(pl, a, nwg, st);
   }
   const int nblk = (int)((pl.N + 255) / 256) > 0 ? (int)((pl.N + 255) / 256) : 1;
   FinArgs f;
   f.targets = targets;
+  f.tgt_i32 = pl.tgt_i32 ? 1 : 0;
   f.N = (int)pl.N;
   f.V = (int)pl.V;
   f.S = pl.S;

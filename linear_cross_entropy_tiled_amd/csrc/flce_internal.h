@@ -15,6 +15,7 @@ struct Plan {
   int dtype, gw_dtype, reduction;
   bool has_bias;
   bool accum_gw, accum_gb;       // backward adds into grad_weight / grad_bias
+  bool tgt_i32;                  // targets are int32 (else int64)
   float scale, cap, z_loss;
 
   int64_t n_tt, n_vt, n_ht;      // 256-wide tiles over tokens, vocabulary, hidden
@@ -34,6 +35,9 @@ struct Plan {
 };
 
 constexpr size_t kStatusBytes = 256;   // status word at workspace offset 0
+// Backward: the dlogits scale factor and its inverse (two fp32 words) follow
+// the status word.  Powers of two: 1 except for fp16 dlogits (bwd_prep_kernel).
+constexpr size_t kDscaleOffset = 16;
 
 // Partial sums of one finalize block (forward).
 struct BlockPart {
@@ -48,11 +52,11 @@ struct BlockPart {
 int make_plan(const flce_params* p, Plan* plan);
 
 hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
-                          const int64_t* targets, float* loss, float* lse, int64_t* num_correct,
+                          const void* targets, float* loss, float* lse, int64_t* num_correct,
                           float* entropy_sum, char* ws, hipStream_t st);
 
 hipError_t launch_backward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
-                           const int64_t* targets, const float* lse, const float* grad_loss,
+                           const void* targets, const float* lse, const float* grad_loss,
                            void* grad_hidden, void* grad_weight, void* grad_bias, char* ws,
                            hipStream_t st);
 

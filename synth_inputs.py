@@ -11,8 +11,10 @@ one recipe never moves another stream.
 
 bf16 inputs are drawn as float32 normals and rounded to bfloat16 with
 round-to-nearest-even; they are carried as their 16-bit patterns
-(``np.uint16``).  ``widen`` turns them (or fp32 arrays) into the exact float64
-values that the oracle consumes.
+(``np.uint16``).  fp16 inputs are the same normals rounded by numpy's
+float32 -> float16 cast (also round-to-nearest-even) and carried as
+``np.float16``.  ``widen`` turns any of them into the exact float64 values
+that the oracle consumes.
 """
 from __future__ import annotations
 
@@ -30,7 +32,7 @@ class Workload:
     n_tokens: int
     hidden: int
     vocab: int
-    dtype: str                      # "f32" | "bf16"
+    dtype: str                      # "f32" | "bf16" | "f16"
     weight_std: float
     bias_std: Optional[float]       # None -> no bias
     logit_scale: float = 1.0
@@ -62,6 +64,11 @@ WORKLOADS = {
     "bf16_n16384_h2048_v256000": Workload(
         "bf16_n16384_h2048_v256000", 16384, 2048, 256000, "bf16", 0.02, None,
         reduction="none", grad_weight_dtype="f32", seed=4),
+    # the headline case with fp16 inputs (fp16 is one of the input types the
+    # fused-linear-ce signature lists), for the fp16 path's parity and timing
+    "f16_n8192_h4096_v128256": Workload(
+        "f16_n8192_h4096_v128256", 8192, 4096, 128256, "f16", 0.02, 0.1,
+        logit_scale=0.5, softcap=30.0, ignore_frac=0.05, reduction="sum", seed=5),
 }
 HEADLINE = "bf16_n8192_h4096_v128256"
 
@@ -85,7 +92,7 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def widen(arr: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
-    """Exact float64 copy of an input array (bf16 bit patterns or float32)."""
+    """Exact float64 copy of an input array (bf16 bit patterns, float16 or float32)."""
     if arr is None:
         return None
     if dtype == "bf16":
@@ -104,6 +111,8 @@ def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarr
         out32 *= np.float32(std)
     if dtype == "bf16":
         return round_to_bf16_bits(out32)
+    if dtype == "f16":
+        return out32.astype(np.float16)
     return out32
 
 
@@ -127,7 +136,7 @@ def make_inputs(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
                 reduction: str = "mean", seed: int = 0) -> dict:
     """Draw one problem.  Returns numpy arrays:
 
-    hidden (N,H), weight (V,H), bias (V,) or None -- uint16 bf16 patterns or float32;
+    hidden (N,H), weight (V,H), bias (V,) or None -- uint16 bf16 patterns, float16 or float32;
     targets (N,) int64 with exactly floor(ignore_frac*N) entries set to -100;
     grad_loss: float32 scalar 1.0 for sum/mean, (N,) N(0,1) for "none".
     """

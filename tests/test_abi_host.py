@@ -70,7 +70,7 @@ def test_workspace_sizes(lib):
     ("dtype", 7, flce.FLCE_ERR_INVALID_ARG),
     ("grad_weight_dtype", 9, flce.FLCE_ERR_INVALID_ARG),
     ("reduction", 3, flce.FLCE_ERR_INVALID_ARG),
-    ("flags", 4, flce.FLCE_ERR_INVALID_ARG),
+    ("flags", 8, flce.FLCE_ERR_INVALID_ARG),
     ("z_loss", -1.0, flce.FLCE_ERR_INVALID_ARG),
     ("logit_scale", float("inf"), flce.FLCE_ERR_INVALID_ARG),
 ])
@@ -80,6 +80,18 @@ def test_bad_params_rejected(lib, field, value, code):
     assert _ws(p, flce.FLCE_PASS_FORWARD)[0] == code
     rc = lib.flce_forward(ctypes.byref(p), 16, 16, None, 16, 16, 16, None, None, 16, 1 << 30, None)
     assert rc == code
+
+
+def test_fp16_and_int32_targets_accepted(lib):
+    """fp16 inputs plan like bf16 (same element size); int32 targets are a flag."""
+    for pass_ in (flce.FLCE_PASS_FORWARD, flce.FLCE_PASS_BACKWARD):
+        pb = flce.make_params(5000, 1024, 50000, dtype="bf16", reduction="mean")
+        ph = flce.make_params(5000, 1024, 50000, dtype="f16", reduction="mean", targets_int32=True)
+        pg = flce.make_params(5000, 1024, 50000, dtype="f16", grad_weight_dtype="f32")
+        rb, rh, rg = _ws(pb, pass_), _ws(ph, pass_), _ws(pg, pass_)
+        assert rb[0] == rh[0] == rg[0] == 0
+        assert rb[1] == rh[1] == rg[1] > 0
+    assert flce.make_params(8, 8, 8, targets_int32=True).flags == flce.FLCE_TARGETS_INT32
 
 
 def test_null_and_misaligned_pointers_rejected(lib):

@@ -69,6 +69,16 @@ SMALL_CASES = [
          weight_std=0.1),
     Case("zipf_targets_zloss", 1024, 256, 5000, "bf16", None, 1.0, None, 1e-4, 0.0, "mean",
          targets="zipf", weight_std=0.05),
+    # fp16 inputs: the same ragged shapes and options, fp16 or fp32 grad_weight
+    Case("ragged_f16_all_options", 700, 200, 1500, "f16", 0.1, 0.7, 2.0, 0.01, 0.1, "mean",
+         weight_std=0.1),
+    Case("ragged_f16_none_gwf32", 333, 136, 777, "f16", None, 1.0, None, 0.0, 0.05, "none", "f32",
+         weight_std=0.1),
+    # fp16 with "mean" over ~1350 valid rows and V = 40000 (two vocabulary
+    # chunks): the off-target logit gradients are ~2e-8, below fp16's smallest
+    # subnormal, unless the backward scales them (a dropped scale fails here)
+    Case("f16_mean_small_gradients", 1500, 128, 40000, "f16", 0.1, 1.0, None, 1e-3, 0.1, "mean",
+         weight_std=0.05),
 ]
 
 
@@ -118,8 +128,8 @@ def _ws_probe(flce, d):
     """A freshly written forward workspace whose status word reflects `d`'s targets."""
     import torch
     n, h = d["hidden"].shape
-    p = flce.make_params(n, h, d["weight"].shape[0], dtype="bf16" if d["hidden"].dtype == torch.bfloat16 else "f32",
-                         reduction="sum")
+    dt = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[d["hidden"].dtype]
+    p = flce.make_params(n, h, d["weight"].shape[0], dtype=dt, reduction="sum")
     ws = torch.empty(flce.flce_workspace_size(p, flce.FLCE_PASS_FORWARD), dtype=torch.uint8,
                      device=d["hidden"].device)
     loss, lse, _ = flce.forward(d["hidden"], d["weight"], d["targets"], d["bias"], reduction="sum",
@@ -323,7 +333,7 @@ def _sampled_check(flce, wl: si.Workload, n_rows=512, n_vocab=512):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["bf16_n8192_h4096_v128256", "bf16_n16384_h2048_v256000",
-                                  "bf16_n8192_h4096_v32000_zipf"])
+                                  "bf16_n8192_h4096_v32000_zipf", "f16_n8192_h4096_v128256"])
 def test_full_size_sampled(flce_lib, name):
     _sampled_check(flce_lib, si.WORKLOADS[name])
 
@@ -340,3 +350,41 @@ RAGGED_MID = si.Workload("bf16_n6000_h1600_v50257_ragged", 6000, 1600, 50257, "b
 @pytest.mark.slow
 def test_ragged_mid_size_sampled(flce_lib):
     _sampled_check(flce_lib, RAGGED_MID)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_int32_targets_match_int64(flce_lib, dtype):
+    """int32 targets (FLCE_TARGETS_INT32) give bit-identical results to the same targets as int64."""
+    import torch
+    c = Case("int32_targets", 700, 200, 1500, dtype, 0.1, 0.7, 2.0, 0.01, 0.1, "mean", weight_std=0.1)
+    inp = _inputs(c)
+    d = to_device(inp, c.dtype)
+    r64 = _run_gpu(flce_lib, c, d)
+    d32 = dict(d)
+    d32["targets"] = d["targets"].to(torch.int32)
+    r32 = _run_gpu(flce_lib, c, d32)
+    for name, a, b in zip(("loss", "lse", "grad_hidden", "grad_weight", "grad_bias"),
+                          (r64[0], r64[1], r64[3], r64[4], r64[5]), (r32[0], r32[1], r32[3], r32[4], r32[5])):
+        assert torch.equal(a, b), name
+    assert r64[2]["num_correct_tokens"].item() == r32[2]["num_correct_tokens"].item()
+    assert torch.equal(r64[2]["entropy_sum"], r32[2]["entropy_sum"])
+    X, W, B, T = widened(inp, c.dtype)
+    fwd = oracle.forward(X, W, B, T, **_opts(c))
+    assert_loss_close(t2np(r32[0]), fwd.loss, c.dtype, "loss")
+
+
+def test_f16_small_gradients_keep_precision(flce_lib):
+    """fp16 logit gradients under "mean" with V = 40000: the entries are ~2e-8, below fp16's
+    subnormals; rounded unscaled they put grad_bias and grad_hidden off by ~1.2e-2 of their
+    maximum (an fp64 emulation of that rounding), scaled by a power of two by ~3e-4.  Bound
+    2e-3 separates the two with a wide margin."""
+    c = Case("f16_mean_small_gradients", 1500, 128, 40000, "f16", 0.1, 1.0, None, 1e-3, 0.1, "mean",
+             weight_std=0.05)
+    inp = _inputs(c)
+    d = to_device(inp, c.dtype)
+    loss, lse, met, gh, gw, gb = _run_gpu(flce_lib, c, d)
+    X, W, B, T = widened(inp, c.dtype)
+    _, rgh, rgw, rgb = oracle.forward_backward(X, W, B, T, inp["grad_loss"].astype(np.float64), **_opts(c))
+    for what, a, r in (("grad_hidden", t2np(gh), rgh), ("grad_weight", t2np(gw), rgw), ("grad_bias", t2np(gb), rgb)):
+        err = np.abs(a - r).max() / np.abs(r).max()
+        assert err <= 2e-3, f"{what}: {err:.3e}"
