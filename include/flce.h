@@ -56,7 +56,8 @@ typedef enum {
                                          under 2^30, H under 2^20                             */
   FLCE_ERR_WORKSPACE_TOO_SMALL = -3,
   FLCE_ERR_HIP = -4,                  /* a HIP runtime call failed                           */
-  FLCE_ERR_TARGET_OUT_OF_RANGE = -5   /* reported by flce_get_status only                    */
+  FLCE_ERR_TARGET_OUT_OF_RANGE = -5,  /* reported by flce_get_status only                    */
+  FLCE_ERR_CALLBACK = -6              /* a chunk loss function returned non-zero             */
 } flce_status;
 
 typedef enum { FLCE_F32 = 0, FLCE_BF16 = 1, FLCE_F16 = 2 } flce_dtype;
@@ -148,6 +149,72 @@ int flce_get_status(const void* workspace, void* stream);
 
 /* Static text for a status code. */
 const char* flce_status_string(int status);
+
+/* ---------------------------------------------------------------------------
+ * Generic chunked linear loss ("Chunked Linear Loss" page: the per-chunk steps
+ * of "Why chunk the projection?" and the "Loss function contract").  The
+ * projection logits = inputs . weight^T is formed one block of rows at a time;
+ * a loss function supplied by the caller turns each block of logits into its
+ * loss and its logits gradient G; the library then adds G . weight to
+ * grad_inputs and G^T . inputs to grad_weight.  No bias, scale or cap: those
+ * belong to the loss function.  At most one block of logits exists at a time.
+ * ------------------------------------------------------------------------- */
+
+/* Called on the host once per block, in row order.  `logits` is device memory
+ * holding the block's (rows, vocab) logits in `dtype` (flce_dtype), row stride
+ * `ld` elements, rows row0 .. row0+rows-1 of inputs.  The function must enqueue
+ * on `stream` work that overwrites logits[i][j] (i < rows, j < vocab) with
+ * d loss / d logits[i][j] in the same dtype, leaves the rest of the buffer as it
+ * is, and adds the block's loss to *loss (device fp32).  Return 0, or non-zero
+ * to stop: flce_chunked_linear_loss then returns FLCE_ERR_CALLBACK and the
+ * outputs are undefined. */
+typedef int (*flce_chunk_loss_fn)(void* user, int64_t row0, int64_t rows, int64_t vocab, void* logits,
+                                  int64_t ld, int32_t dtype, float* loss, void* stream);
+
+typedef struct {
+  int64_t n_tokens;           /* N >= 0                                                  */
+  int64_t hidden;             /* H >= 8, H % 8 == 0                                      */
+  int64_t vocab;              /* V >= 1                                                  */
+  int64_t chunk_rows;         /* rows per block, a multiple of 256; 0 = library choice   */
+  int32_t dtype;              /* flce_dtype of inputs, weight, logits and grad_inputs    */
+  int32_t grad_weight_dtype;  /* flce_dtype of grad_weight                               */
+  int32_t accum_dtype;        /* grad_weight summed over the blocks in FLCE_F32 (rounded
+                                 once) or in grad_weight_dtype (rounded per block):
+                                 "Chunked Linear Loss", "Weight-gradient accumulation
+                                 dtype", its "fp32" and "weight" modes                   */
+  int32_t flags;              /* FLCE_ACCUMULATE_GRAD_WEIGHT or 0                        */
+} flce_chunked_params;
+
+/* Bytes of device workspace flce_chunked_linear_loss needs.  Host only. */
+int flce_chunked_workspace_size(const flce_chunked_params* p, size_t* bytes);
+
+/*
+ *  inputs:      device (N, H), weight: device (V, H), both in p->dtype.
+ *  loss:        device fp32 scalar: the sum of the blocks' losses.  Required.
+ *  grad_inputs: device (N, H) in p->dtype (fp32 accumulation, one rounding).
+ *  grad_weight: device (V, H) in p->grad_weight_dtype.
+ * The loss function runs between launches on `stream`; with a deterministic
+ * loss function the results are deterministic.
+ */
+int flce_chunked_linear_loss(const flce_chunked_params* p, const void* inputs, const void* weight,
+                             flce_chunk_loss_fn fn, void* user, float* loss, void* grad_inputs,
+                             void* grad_weight, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Built-in loss function for flce_chunked_linear_loss: weighted squared error,
+ * the "Direct logits gradients" example of the "Chunked Linear Loss" page:
+ *   loss = sum_ij (z_ij - y_ij)^2 r_i f_j,   d loss / d z_ij = 2 (z_ij - y_ij) r_i f_j,
+ * with z the logits (read in their dtype, math in fp32) and the gradient
+ * rounded to the logits' dtype.  `user` points to an flce_wmse_args. */
+typedef struct {
+  const float* target;          /* device (N, vocab) fp32, row stride ld_target >= vocab   */
+  int64_t ld_target;
+  const float* row_weight;      /* device (N) fp32 (r)                                     */
+  const float* feature_weight;  /* device (vocab) fp32 (f)                                 */
+  float* row_loss;              /* device (N) fp32: receives each row's loss               */
+} flce_wmse_args;
+
+int flce_weighted_mse_chunk(void* user, int64_t row0, int64_t rows, int64_t vocab, void* logits, int64_t ld,
+                            int32_t dtype, float* loss, void* stream);
 
 /* Library version, major*10000 + minor*100 + patch. */
 int flce_version(void);

@@ -7,7 +7,10 @@ declared in ``include/flce.h``).  This module only marshals arguments:
   ``flce_get_status``, ``flce_status_string``, ``flce_version`` mirror the C
   entry points one to one and take raw device pointers (ints);
 * ``forward`` / ``backward`` are torch conveniences that allocate outputs and
-  the workspace with torch and pass the current HIP stream.
+  the workspace with torch and pass the current HIP stream;
+* ``chunked_linear_loss`` / ``weighted_mse`` drive the generic chunked loss
+  (``flce_chunked_linear_loss``) with a Python loss function or the built-in
+  weighted squared error (``flce_weighted_mse_chunk``).
 
 There is no fallback: if the library is missing, ``load()`` raises.
 """
@@ -27,6 +30,7 @@ FLCE_ERR_UNSUPPORTED = -2
 FLCE_ERR_WORKSPACE_TOO_SMALL = -3
 FLCE_ERR_HIP = -4
 FLCE_ERR_TARGET_OUT_OF_RANGE = -5
+FLCE_ERR_CALLBACK = -6
 
 FLCE_F32 = 0
 FLCE_BF16 = 1
@@ -40,7 +44,8 @@ FLCE_ACCUMULATE_GRAD_BIAS = 2
 FLCE_TARGETS_INT32 = 4
 
 EXPORTED = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_get_status",
-            "flce_status_string", "flce_version")
+            "flce_status_string", "flce_version", "flce_chunked_workspace_size",
+            "flce_chunked_linear_loss", "flce_weighted_mse_chunk")
 
 
 class flce_params(ctypes.Structure):
@@ -58,6 +63,35 @@ class flce_params(ctypes.Structure):
         ("z_loss", ctypes.c_float),
         ("reserved_f", ctypes.c_float),
     ]
+
+
+class flce_chunked_params(ctypes.Structure):
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64),
+        ("hidden", ctypes.c_int64),
+        ("vocab", ctypes.c_int64),
+        ("chunk_rows", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("grad_weight_dtype", ctypes.c_int32),
+        ("accum_dtype", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+    ]
+
+
+class flce_wmse_args(ctypes.Structure):
+    _fields_ = [
+        ("target", ctypes.c_void_p),
+        ("ld_target", ctypes.c_int64),
+        ("row_weight", ctypes.c_void_p),
+        ("feature_weight", ctypes.c_void_p),
+        ("row_loss", ctypes.c_void_p),
+    ]
+
+
+# int fn(void* user, int64 row0, int64 rows, int64 vocab, void* logits, int64 ld, int32 dtype,
+#        float* loss, void* stream)
+CHUNK_LOSS_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p)
 
 
 class FlceError(RuntimeError):
@@ -93,6 +127,14 @@ def load(path: Optional[str] = None):
     lib.flce_status_string.restype = ctypes.c_char_p
     lib.flce_version.argtypes = []
     lib.flce_version.restype = ctypes.c_int
+    CP = ctypes.POINTER(flce_chunked_params)
+    lib.flce_chunked_workspace_size.argtypes = [CP, ctypes.POINTER(sz)]
+    lib.flce_chunked_workspace_size.restype = ctypes.c_int
+    lib.flce_chunked_linear_loss.argtypes = [CP, vp, vp, CHUNK_LOSS_FN, vp, vp, vp, vp, vp, sz, vp]
+    lib.flce_chunked_linear_loss.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.flce_weighted_mse_chunk.argtypes = [vp, i64, i64, i64, vp, i64, ctypes.c_int32, vp, vp]
+    lib.flce_weighted_mse_chunk.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -118,6 +160,25 @@ def flce_backward(params, hidden, weight, bias, targets, lse, grad_loss, grad_hi
     return load().flce_backward(ctypes.byref(params), hidden, weight, bias, targets, lse, grad_loss,
                                 grad_hidden, grad_weight, grad_bias, workspace, workspace_bytes,
                                 stream)
+
+
+def flce_chunked_workspace_size(params: flce_chunked_params) -> int:
+    out = ctypes.c_size_t(0)
+    rc = load().flce_chunked_workspace_size(ctypes.byref(params), ctypes.byref(out))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_chunked_workspace_size")
+    return out.value
+
+
+def flce_chunked_linear_loss(params, inputs, weight, fn, user, loss, grad_inputs, grad_weight, workspace,
+                             workspace_bytes, stream) -> int:
+    return load().flce_chunked_linear_loss(ctypes.byref(params), inputs, weight, fn, user, loss, grad_inputs,
+                                           grad_weight, workspace, workspace_bytes, stream)
+
+
+def weighted_mse_chunk_fn():
+    """The library's built-in loss function (flce_weighted_mse_chunk) as a CHUNK_LOSS_FN."""
+    return ctypes.cast(load().flce_weighted_mse_chunk, CHUNK_LOSS_FN)
 
 
 def flce_get_status(workspace, stream) -> int:
@@ -270,3 +331,126 @@ def backward(hidden, weight, targets, lse, grad_loss, bias=None, *, logit_scale:
 
 def get_status(workspace) -> int:
     return flce_get_status(_ptr(workspace), _stream_handle(workspace.device))
+
+
+# ----------------------------------------------------------------------------- generic chunked loss
+
+def make_chunked_params(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
+                        grad_weight_dtype: Optional[str] = None, grad_weight_accum_dtype: str = "fp32",
+                        chunk_rows: int = 0, accumulate_grad_weight: bool = False) -> flce_chunked_params:
+    if grad_weight_accum_dtype not in ("fp32", "weight"):
+        raise ValueError(f"invalid grad_weight_accum_dtype {grad_weight_accum_dtype!r}")
+    p = flce_chunked_params()
+    p.n_tokens, p.hidden, p.vocab, p.chunk_rows = n_tokens, hidden, vocab, chunk_rows
+    p.dtype = DTYPES[dtype]
+    p.grad_weight_dtype = DTYPES[grad_weight_dtype or dtype]
+    p.accum_dtype = FLCE_F32 if grad_weight_accum_dtype == "fp32" else p.grad_weight_dtype
+    p.flags = FLCE_ACCUMULATE_GRAD_WEIGHT if accumulate_grad_weight else 0
+    return p
+
+
+def _run_chunked(inputs, weight, fn, user, *, chunk_rows, grad_weight_dtype, grad_weight_accum_dtype,
+                 grad_weight, workspace, on_error=None):
+    import torch
+    _check(inputs, "inputs")
+    _check(weight, "weight")
+    _check(grad_weight, "grad_weight")
+    n, h = inputs.shape
+    v = weight.shape[0]
+    dt = _dtype_name(inputs)
+    if grad_weight is not None:
+        grad_weight_dtype = _dtype_name(grad_weight)
+        if tuple(grad_weight.shape) != (v, h):
+            raise ValueError("grad_weight must have the weight's shape")
+    p = make_chunked_params(n, h, v, dtype=dt, grad_weight_dtype=grad_weight_dtype,
+                            grad_weight_accum_dtype=grad_weight_accum_dtype, chunk_rows=chunk_rows,
+                            accumulate_grad_weight=grad_weight is not None)
+    dev = inputs.device
+    ws_bytes = flce_chunked_workspace_size(p)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    gi = torch.empty((n, h), dtype=inputs.dtype, device=dev)
+    gw = grad_weight if grad_weight is not None else torch.empty((v, h), dtype=tdt[grad_weight_dtype or dt], device=dev)
+    rc = flce_chunked_linear_loss(p, _ptr(inputs), _ptr(weight), fn, user, _ptr(loss), _ptr(gi), _ptr(gw),
+                                  _ptr(workspace), workspace.numel(), _stream_handle(dev))
+    if rc == FLCE_ERR_CALLBACK and on_error is not None and on_error[0] is not None:
+        raise on_error[0]
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_chunked_linear_loss")
+    return loss.reshape(()), gi, gw
+
+
+def chunked_linear_loss(inputs, weight, loss_and_grad_fn, *args, chunk_rows: int = 0,
+                        grad_weight_dtype: Optional[str] = None, grad_weight_accum_dtype: str = "fp32",
+                        grad_weight=None, workspace=None, **kwargs):
+    """Generic chunked linear loss with a Python loss function.
+
+    ``loss_and_grad_fn(logits_chunk, *chunk_args, **chunk_kwargs) -> (loss, grad_logits)`` sees one
+    block of rows of ``inputs @ weight.T`` (in the inputs' dtype) and returns the block's scalar loss
+    and the gradient of the logits (same shape).  Tensor arguments whose leading dimension is N are
+    sliced to the block's rows; others are passed through.  Returns (loss, grad_inputs, grad_weight);
+    with ``grad_weight`` given, the weight gradient is added to it in place."""
+    import torch
+    n = inputs.shape[0]
+    ws_holder = {}
+    err = [None]
+
+    def slice_arg(a, r0, rows):
+        if isinstance(a, torch.Tensor) and a.dim() > 0 and a.shape[0] == n:
+            return a[r0:r0 + rows]
+        return a
+
+    def cb(user, row0, rows, vocab, logits_ptr, ld, dtype, loss_ptr, stream):
+        try:
+            ws = ws_holder["ws"]
+            esize = 4 if dtype == FLCE_F32 else 2
+            off = logits_ptr - ws.data_ptr()
+            tdt = {FLCE_F32: torch.float32, FLCE_BF16: torch.bfloat16, FLCE_F16: torch.float16}[dtype]
+            buf = ws[off:off + rows * ld * esize].view(tdt).view(rows, ld)[:, :vocab]
+            c_args = [slice_arg(a, row0, rows) for a in args]
+            c_kwargs = {k: slice_arg(a, row0, rows) for k, a in kwargs.items()}
+            loss, grad = loss_and_grad_fn(buf, *c_args, **c_kwargs)
+            buf.copy_(grad)
+            ws_holder["loss"].add_(loss.reshape(1).to(torch.float32))
+            return 0
+        except Exception as e:   # reported after the library returns
+            err[0] = e
+            return 1
+
+    fn = CHUNK_LOSS_FN(cb)
+    h = inputs.shape[1]
+    v = weight.shape[0]
+    p = make_chunked_params(n, h, v, dtype=_dtype_name(inputs), grad_weight_dtype=grad_weight_dtype,
+                            grad_weight_accum_dtype=grad_weight_accum_dtype, chunk_rows=chunk_rows)
+    ws_bytes = flce_chunked_workspace_size(p)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=inputs.device)
+    ws_holder["ws"] = workspace
+    # the callback adds each block's loss to a torch scalar; the library's own loss word is unused
+    ws_holder["loss"] = torch.zeros(1, dtype=torch.float32, device=inputs.device)
+    _, gi, gw = _run_chunked(inputs, weight, fn, None, chunk_rows=chunk_rows, grad_weight_dtype=grad_weight_dtype,
+                             grad_weight_accum_dtype=grad_weight_accum_dtype, grad_weight=grad_weight,
+                             workspace=workspace, on_error=err)
+    return ws_holder["loss"].reshape(()), gi, gw
+
+
+def weighted_mse(inputs, weight, target, row_weight, feature_weight, *, chunk_rows: int = 0,
+                 grad_weight_dtype: Optional[str] = None, grad_weight_accum_dtype: str = "fp32",
+                 grad_weight=None, workspace=None):
+    """Generic chunked linear loss with the built-in weighted squared error:
+    loss = sum_ij (z_ij - target_ij)^2 row_weight_i feature_weight_j, z = inputs @ weight.T.
+    ``target`` is (N, V) fp32 with contiguous rows, the weights fp32 vectors."""
+    import torch
+    for t, nme in ((target, "target"), (row_weight, "row_weight"), (feature_weight, "feature_weight")):
+        if t.dtype != torch.float32 or not t.is_cuda:
+            raise ValueError(f"{nme} must be a float32 device tensor")
+    if target.stride(1) != 1 or not row_weight.is_contiguous() or not feature_weight.is_contiguous():
+        raise ValueError("target rows, row_weight and feature_weight must be contiguous")
+    row_loss = torch.empty(inputs.shape[0], dtype=torch.float32, device=inputs.device)
+    a = flce_wmse_args(_ptr(target), target.stride(0), _ptr(row_weight), _ptr(feature_weight), _ptr(row_loss))
+    return _run_chunked(inputs, weight, weighted_mse_chunk_fn(), ctypes.cast(ctypes.pointer(a), ctypes.c_void_p),
+                        chunk_rows=chunk_rows, grad_weight_dtype=grad_weight_dtype,
+                        grad_weight_accum_dtype=grad_weight_accum_dtype, grad_weight=grad_weight,
+                        workspace=workspace)

@@ -19,6 +19,19 @@ static constexpr size_t kGhPartBudget = size_t(256) << 20;
 // Number of compute units the forward split count is sized for (MI355X).
 static constexpr int64_t kTargetWorkgroups = 256;
 
+void plan_gh_split(int64_t tiles, int64_t cvn, int esize, int64_t N, int64_t H, int* parts_out, int* kt_out) {
+  const int64_t stages = cvn * esize / 128;   // K stages of 128 bytes per row
+  int64_t parts = tiles > 0 ? (kTargetWorkgroups + tiles - 1) / tiles : 1;
+  if (parts > stages / kMinStagesPerPart) parts = stages / kMinStagesPerPart;
+  const int64_t per_part_bytes = N * H * 4;
+  if (per_part_bytes > 0 && parts > (int64_t)(kGhPartBudget / per_part_bytes))
+    parts = (int64_t)(kGhPartBudget / per_part_bytes);
+  if (parts < 2 || tiles >= kTargetWorkgroups / 2) parts = 1;
+  const int64_t kt = (stages + parts - 1) / parts;
+  *kt_out = (int)kt;
+  *parts_out = (int)((stages + kt - 1) / kt);
+}
+
 int make_plan(const flce_params* p, Plan* pl) {
   if (!p || !pl) return FLCE_ERR_INVALID_ARG;
   if (p->n_tokens < 0 || p->hidden <= 0 || p->vocab <= 0) return FLCE_ERR_INVALID_ARG;
@@ -88,18 +101,7 @@ int make_plan(const flce_params* p, Plan* pl) {
   // grad_hidden has only n_ht x n_tt output tiles; when that is well under one
   // workgroup per CU, split each chunk's contraction (K = vocabulary rows) and
   // add the fp32 partials in a fixed order afterwards
-  {
-    const int64_t tiles = P.n_ht * P.n_tt;
-    const int64_t stages = P.Vc * esize / 128;   // K stages of 128 bytes per row
-    int64_t parts = tiles > 0 ? (kTargetWorkgroups + tiles - 1) / tiles : 1;
-    if (parts > stages / kMinStagesPerPart) parts = stages / kMinStagesPerPart;
-    const int64_t per_part_bytes = P.N * P.H * 4;
-    if (per_part_bytes > 0 && parts > (int64_t)(kGhPartBudget / per_part_bytes))
-      parts = (int64_t)(kGhPartBudget / per_part_bytes);
-    if (parts < 2 || tiles >= kTargetWorkgroups / 2) parts = 1;
-    P.gh_kt_per_part = (int)((stages + parts - 1) / parts);
-    P.gh_parts = (int)((stages + P.gh_kt_per_part - 1) / P.gh_kt_per_part);
-  }
+  plan_gh_split(P.n_ht * P.n_tt, P.Vc, esize, P.N, P.H, &P.gh_parts, &P.gh_kt_per_part);
   size_t o = kStatusBytes;
   P.b_coefA = o;
   o = align_up(o + size_t(P.N_pad) * 4, 256);
@@ -125,6 +127,81 @@ int make_plan(const flce_params* p, Plan* pl) {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Logits block budget of the generic chunked loss: rows per block so that
+// rows x V_pad elements stay within it (and within 32-bit offsets).
+static constexpr size_t kLogitsBlockBudget = size_t(1) << 30;
+
+static bool valid_dtype(int d) { return d == FLCE_F32 || d == FLCE_BF16 || d == FLCE_F16; }
+
+int make_chunk_plan(const flce_chunked_params* p, ChunkPlan* pl) {
+  if (!p || !pl) return FLCE_ERR_INVALID_ARG;
+  if (p->n_tokens < 0 || p->hidden <= 0 || p->vocab <= 0 || p->chunk_rows < 0) return FLCE_ERR_INVALID_ARG;
+  if (!valid_dtype(p->dtype) || !valid_dtype(p->grad_weight_dtype)) return FLCE_ERR_INVALID_ARG;
+  if (p->accum_dtype != FLCE_F32 && p->accum_dtype != p->grad_weight_dtype) return FLCE_ERR_INVALID_ARG;
+  if ((p->flags & ~FLCE_ACCUMULATE_GRAD_WEIGHT) != 0) return FLCE_ERR_INVALID_ARG;
+  if (p->hidden % 8 != 0 || p->chunk_rows % 256 != 0) return FLCE_ERR_UNSUPPORTED;
+  if (p->n_tokens > (int64_t(1) << 30) || p->vocab > (int64_t(1) << 30) || p->hidden > (int64_t(1) << 20))
+    return FLCE_ERR_UNSUPPORTED;
+  const int esize = p->dtype == FLCE_F32 ? 4 : 2;
+  if (p->n_tokens * p->hidden * 4 >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+
+  ChunkPlan& P = *pl;
+  memset(&P, 0, sizeof(P));
+  P.N = p->n_tokens;
+  P.H = p->hidden;
+  P.V = p->vocab;
+  P.dtype = p->dtype;
+  P.gw_dtype = p->grad_weight_dtype;
+  P.esize = esize;
+  P.accum_gw = (p->flags & FLCE_ACCUMULATE_GRAD_WEIGHT) != 0;
+  P.n_ht = (P.H + 255) / 256;
+  P.n_vt = (P.V + 255) / 256;
+  P.V_pad = P.n_vt * 256;
+  const int64_t row_bytes = P.V_pad * esize;
+  int64_t rows = p->chunk_rows;
+  if (rows == 0) {
+    rows = (int64_t)(kLogitsBlockBudget / (size_t)row_bytes) / 256 * 256;
+    const int64_t n_pad = (P.N + 255) / 256 * 256;
+    if (rows > n_pad) rows = n_pad;
+    if (rows < 256) rows = 256;
+  }
+  if (rows * row_bytes >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+  P.rows_c = rows;
+  P.n_chunks = P.N > 0 ? (int)((P.N + rows - 1) / rows) : 0;
+  // vocabulary chunks of the grad_inputs contraction: weight rows x H within 32-bit offsets
+  int64_t vc = ((int64_t(1) << 31) - 1) / (P.H * esize) / 256 * 256;
+  if (vc < 256) return FLCE_ERR_UNSUPPORTED;
+  if (vc > P.V_pad) vc = P.V_pad;
+  P.Vc = vc;
+  P.n_vchunks = (int)((P.V_pad + vc - 1) / vc);
+  P.gw_acc32 = p->accum_dtype == FLCE_F32 && P.gw_dtype != FLCE_F32 && P.n_chunks > 1;
+
+  size_t o = kStatusBytes;
+  P.b_L = o;
+  o = align_up(o + size_t(rows) * row_bytes, 256);
+  P.b_xt = o;
+  o = align_up(o + size_t(P.H) * rows * esize, 256);
+  P.b_giacc = o;
+  if (P.dtype != FLCE_F32 && P.n_vchunks > 1) o = align_up(o + size_t(rows) * P.H * 4, 256);
+  P.b_gwacc = o;
+  if (P.gw_acc32) o = align_up(o + size_t(P.V) * P.H * 4, 256);
+  P.b_ghpart = o;
+  {
+    // the largest K split any block asks for (blocks differ only in the last one's rows)
+    int parts = 1, kt = 0, parts2 = 1;
+    plan_gh_split(P.n_ht * (rows / 256), P.Vc, esize, rows, P.H, &parts, &kt);
+    const int64_t last = P.N > 0 ? P.N - (int64_t)(P.n_chunks - 1) * rows : 0;
+    const int64_t last_tt = (last + 255) / 256;
+    plan_gh_split(P.n_ht * last_tt, P.Vc, esize, last, P.H, &parts2, &kt);
+    size_t part_bytes = 0;
+    if (parts > 1) part_bytes = size_t(parts) * rows * P.H * 4;
+    if (parts2 > 1 && size_t(parts2) * last * P.H * 4 > part_bytes) part_bytes = size_t(parts2) * last * P.H * 4;
+    o = align_up(o + part_bytes, 256);
+  }
+  P.b_bytes = o;
+  return FLCE_OK;
+}
+
 }  // namespace flce
 
 using namespace flce;
@@ -141,6 +218,7 @@ const char* flce_status_string(int s) {
     case FLCE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case FLCE_ERR_HIP: return "HIP runtime error";
     case FLCE_ERR_TARGET_OUT_OF_RANGE: return "a target is outside [0, vocab) and not ignore_index";
+    case FLCE_ERR_CALLBACK: return "the chunk loss function reported an error";
     default: return "unknown status";
   }
 }
@@ -196,6 +274,47 @@ int flce_backward(const flce_params* p, const void* hidden, const void* weight, 
                                  grad_weight, grad_bias, static_cast<char*>(workspace),
                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+int flce_chunked_workspace_size(const flce_chunked_params* p, size_t* bytes) {
+  if (!bytes) return FLCE_ERR_INVALID_ARG;
+  ChunkPlan pl;
+  const int rc = make_chunk_plan(p, &pl);
+  if (rc != FLCE_OK) return rc;
+  *bytes = pl.b_bytes;
+  return FLCE_OK;
+}
+
+int flce_chunked_linear_loss(const flce_chunked_params* p, const void* inputs, const void* weight,
+                             flce_chunk_loss_fn fn, void* user, float* loss, void* grad_inputs,
+                             void* grad_weight, void* workspace, size_t workspace_bytes, void* stream) {
+  ChunkPlan pl;
+  const int rc = make_chunk_plan(p, &pl);
+  if (rc != FLCE_OK) return rc;
+  if (!fn || !loss || !weight || !grad_weight || !workspace) return FLCE_ERR_INVALID_ARG;
+  if (pl.N > 0 && (!inputs || !grad_inputs)) return FLCE_ERR_INVALID_ARG;
+  if (!aligned16(inputs) || !aligned16(weight) || !aligned16(grad_inputs) || !aligned16(grad_weight) ||
+      !aligned16(workspace))
+    return FLCE_ERR_UNSUPPORTED;
+  if (workspace_bytes < pl.b_bytes) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  return launch_chunked(pl, inputs, weight, fn, user, loss, grad_inputs, grad_weight,
+                        static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+int flce_weighted_mse_chunk(void* user, int64_t row0, int64_t rows, int64_t vocab, void* logits, int64_t ld,
+                            int32_t dtype, float* loss, void* stream) {
+  const flce_wmse_args* a = static_cast<const flce_wmse_args*>(user);
+  if (!a || !a->target || !a->row_weight || !a->feature_weight || !a->row_loss || !logits || !loss)
+    return FLCE_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype) || row0 < 0 || rows < 0 || vocab <= 0 || ld < vocab || a->ld_target < vocab)
+    return FLCE_ERR_INVALID_ARG;
+  const uintptr_t fa = reinterpret_cast<uintptr_t>(a->target) | reinterpret_cast<uintptr_t>(a->row_weight) |
+                       reinterpret_cast<uintptr_t>(a->feature_weight) | reinterpret_cast<uintptr_t>(a->row_loss);
+  if ((fa & 3) != 0 || ld % 4 != 0 || !aligned16(logits) || rows > (int64_t(1) << 30) ||
+      vocab > (int64_t(1) << 30))
+    return FLCE_ERR_UNSUPPORTED;
+  if (rows == 0) return FLCE_OK;
+  return launch_wmse(*a, row0, (int)rows, (int)vocab, logits, (int)ld, dtype, loss, static_cast<hipStream_t>(stream));
 }
 
 int flce_get_status(const void* workspace, void* stream) {

@@ -365,19 +365,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
 // grad_weight for one chunk: C[h][v] = sum_t hidden[t][h] D[t][v]
 // A = hidden (MNMAJOR: rows t, cols h), B = D (MNMAJOR: rows t, cols v).
 // ---------------------------------------------------------------------------
-struct GwArgs {
-  const char* hiddenT;   // hidden transposed: [H][N_pad], zero past N
-  const char* D;
-  int ldD;
-  int N, H, V, N_pad;
-  int cv0;
-  int n_ht, n_vt_c;
-  void* gw;
-  int gw_type;      // flce_dtype of grad_weight
-  int accumulate;   // add to grad_weight's current contents
-  const float* dscale;   // [1]: 2^-s, undoes the factor D is stored with
-};
-
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void bwd_gw_kernel(GwArgs a) {
   constexpr int E = sizeof(T);
@@ -422,7 +409,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gw_kernel(GwArgs a) {
         const size_t o = (size_t)v * a.H + h;
         float c[4] = {acc[mi][ni][4 * g] * inv, acc[mi][ni][4 * g + 1] * inv, acc[mi][ni][4 * g + 2] * inv,
                       acc[mi][ni][4 * g + 3] * inv};
-        update4(a.gw, o, a.gw_type, a.accumulate != 0, c);
+        if (a.mode == 1 || a.mode == 2) {
+          const f32x4 prev = *reinterpret_cast<const f32x4*>(a.acc32 + o);
+#pragma unroll
+          for (int j = 0; j < 4; j++) c[j] += prev[j];
+        }
+        if (a.mode <= 1) store4(a.acc32 + o, c[0], c[1], c[2], c[3]);
+        else update4(a.gw, o, a.gw_type, a.accumulate != 0, c);
       }
   }
 }
@@ -435,23 +428,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gw_kernel(GwArgs a) {
 // mode 2: last chunk (out = cast(accumulator + C))
 // mode 3: only chunk (out = cast(C))
 // ---------------------------------------------------------------------------
-struct GhArgs {
-  const char* weight;
-  const char* D;
-  int ldD;
-  int N, H, V;
-  int cv0, cvn;     // chunk start and padded width
-  int n_ht, n_tt;
-  float* accb;      // fp32 N x H accumulator (may alias out when out is fp32)
-  void* out;
-  int out_f32;
-  int mode;
-  int parts;        // > 1: K split; split p covers stages [p kt_per_part, (p+1) kt_per_part)
-  int kt_per_part;
-  float* part;      // parts x N x H fp32 partials (parts > 1)
-  const float* dscale;   // [1]: 2^-s, undoes the factor D is stored with
-};
-
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void bwd_gh_kernel(GhArgs a) {
   constexpr int E = sizeof(T);
@@ -612,11 +588,7 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
   bwd_prep_kernel<<<1, 1024, 0, st>>>(pa);
 
   T* hiddenT = reinterpret_cast<T*>(ws + pl.b_xt);
-  if (pl.N > 0) {
-    dim3 grid((unsigned)(pl.N_pad / 64), (unsigned)((pl.H + 63) / 64));
-    transpose_hidden_kernel<T><<<grid, 256, 0, st>>>(reinterpret_cast<const T*>(hidden), (int)pl.N, (int)pl.H,
-                                                     (int)pl.N_pad, hiddenT);
-  }
+  if (pl.N > 0) launch_transpose_hidden(pl.dtype, hidden, (int)pl.N, (int)pl.H, (int)pl.N_pad, hiddenT, st);
   const bool gh_f32 = pl.dtype == FLCE_F32;
   float* accb = gh_f32 ? reinterpret_cast<float*>(grad_hidden) : reinterpret_cast<float*>(ws + pl.b_ghacc);
   const int ldD = (int)pl.Vc;
@@ -674,7 +646,9 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       g.gw_type = pl.gw_dtype;
       g.dscale = dscale;
       g.accumulate = pl.accum_gw ? 1 : 0;
-      bwd_gw_kernel<T><<<(int)pl.n_ht * n_vt_c, kThreads, 0, st>>>(g);
+      g.acc32 = nullptr;
+      g.mode = 3;   // each vocabulary row belongs to one chunk: written once
+      launch_gw(pl.dtype, g, st);
     }
     if (pl.N > 0) {
       GhArgs h;
@@ -696,12 +670,7 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       h.kt_per_part = pl.gh_kt_per_part;
       h.part = reinterpret_cast<float*>(ws + pl.b_ghpart);
       h.dscale = dscale;
-      bwd_gh_kernel<T><<<(int)(pl.n_ht * pl.n_tt) * pl.gh_parts, kThreads, 0, st>>>(h);
-      if (pl.gh_parts > 1) {
-        const int64_t n4 = pl.N * pl.H / 4;
-        bwd_gh_reduce<T><<<(int)((n4 + 255) / 256), 256, 0, st>>>(h.part, pl.gh_parts, n4, pl.N * pl.H, accb,
-                                                                  grad_hidden, gh_f32, h.mode);
-      }
+      launch_gh(pl.dtype, h, st);
     }
   }
   if (grad_bias) {
@@ -710,6 +679,43 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
                                                                pl.accum_gb ? 1 : 0, dscale);
   }
   return hipGetLastError();
+}
+
+template <typename T>
+static void launch_transpose_t(const void* hidden, int N, int H, int N_pad, void* hiddenT, hipStream_t st) {
+  dim3 grid((unsigned)(N_pad / 64), (unsigned)((H + 63) / 64));
+  transpose_hidden_kernel<T><<<grid, 256, 0, st>>>(reinterpret_cast<const T*>(hidden), N, H, N_pad,
+                                                   reinterpret_cast<T*>(hiddenT));
+}
+
+void launch_transpose_hidden(int dtype, const void* hidden, int N, int H, int N_pad, void* hiddenT,
+                             hipStream_t st) {
+  if (dtype == FLCE_BF16) launch_transpose_t<bf16>(hidden, N, H, N_pad, hiddenT, st);
+  else if (dtype == FLCE_F16) launch_transpose_t<f16>(hidden, N, H, N_pad, hiddenT, st);
+  else launch_transpose_t<float>(hidden, N, H, N_pad, hiddenT, st);
+}
+
+void launch_gw(int dtype, const GwArgs& g, hipStream_t st) {
+  const int nwg = g.n_ht * g.n_vt_c;
+  if (dtype == FLCE_BF16) bwd_gw_kernel<bf16><<<nwg, kThreads, 0, st>>>(g);
+  else if (dtype == FLCE_F16) bwd_gw_kernel<f16><<<nwg, kThreads, 0, st>>>(g);
+  else bwd_gw_kernel<float><<<nwg, kThreads, 0, st>>>(g);
+}
+
+template <typename T>
+static void launch_gh_t(const GhArgs& h, hipStream_t st) {
+  bwd_gh_kernel<T><<<h.n_ht * h.n_tt * h.parts, kThreads, 0, st>>>(h);
+  if (h.parts > 1) {
+    const int64_t nh = (int64_t)h.N * h.H, n4 = nh / 4;
+    bwd_gh_reduce<T><<<(int)((n4 + 255) / 256), 256, 0, st>>>(h.part, h.parts, n4, nh, h.accb, h.out, h.out_f32,
+                                                              h.mode);
+  }
+}
+
+void launch_gh(int dtype, const GhArgs& h, hipStream_t st) {
+  if (dtype == FLCE_BF16) launch_gh_t<bf16>(h, st);
+  else if (dtype == FLCE_F16) launch_gh_t<f16>(h, st);
+  else launch_gh_t<float>(h, st);
 }
 
 hipError_t launch_backward(const Plan& pl, const void* hidden, const void* weight, const void* bias,

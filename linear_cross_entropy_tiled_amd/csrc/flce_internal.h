@@ -49,7 +49,83 @@ struct BlockPart {
   int pad;
 };
 
+// ---------------------------------------------------------------------------
+// Gradient contractions, shared by the fused backward (one vocabulary chunk of
+// D per launch) and the generic chunked loss (one block of rows per launch).
+// D is a [rows][ldD] scratch in the input dtype, zero outside the valid
+// rows and columns.
+// ---------------------------------------------------------------------------
+
+// grad_weight[v][:] for the vocabulary rows [cv0, cv0 + 256 n_vt_c):
+// sum over t < N_pad of D[t][v - cv0] hiddenT[:][t], times dscale[1].
+// mode 3: out (+)= C (accumulate), rounded once; with K blocks in several
+// launches: mode 0 acc32 = C, 1 acc32 += C, 2 out (+)= acc32 + C.
+struct GwArgs {
+  const char* hiddenT;   // hidden transposed: [H][N_pad], zero past the valid rows
+  const char* D;
+  int ldD;
+  int N, H, V, N_pad;
+  int cv0;
+  int n_ht, n_vt_c;
+  void* gw;
+  int gw_type;      // flce_dtype of grad_weight
+  int accumulate;   // add to grad_weight's current contents (modes 2, 3)
+  const float* dscale;   // [1]: 2^-s, undoes the factor D is stored with
+  float* acc32;     // fp32 V x H accumulator (modes 0-2)
+  int mode;
+};
+
+// grad_hidden[t][:] = sum over the chunk's vocabulary rows of D[t][v] W[v][:],
+// times dscale[1].  mode 0: first of several chunks (store the fp32
+// accumulator), 1: middle (accumulator += C), 2: last (out = cast(acc + C)),
+// 3: only chunk (out = cast(C)).
+struct GhArgs {
+  const char* weight;
+  const char* D;
+  int ldD;
+  int N, H, V;
+  int cv0, cvn;     // chunk start and padded width
+  int n_ht, n_tt;
+  float* accb;      // fp32 N x H accumulator (may alias out when out is fp32)
+  void* out;
+  int out_f32;
+  int mode;
+  int parts;        // > 1: K split; split p covers stages [p kt_per_part, (p+1) kt_per_part)
+  int kt_per_part;
+  float* part;      // parts x N x H fp32 partials (parts > 1)
+  const float* dscale;   // [1]: 2^-s, undoes the factor D is stored with
+};
+
+// hiddenT[h][t] = hidden[t][h] for t < N, 0 for N <= t < N_pad.
+void launch_transpose_hidden(int dtype, const void* hidden, int N, int H, int N_pad, void* hiddenT,
+                             hipStream_t st);
+void launch_gw(int dtype, const GwArgs& g, hipStream_t st);
+void launch_gh(int dtype, const GhArgs& h, hipStream_t st);
+// grad_hidden K-split planning (parts, 64-row stages per part) for a chunk of
+// width cvn over n_tiles output tiles.
+void plan_gh_split(int64_t n_tiles, int64_t cvn, int esize, int64_t N, int64_t H, int* parts, int* kt_per_part);
+
 int make_plan(const flce_params* p, Plan* plan);
+
+// Generic chunked loss (flce_chunked_linear_loss): blocks of rows_c rows.
+struct ChunkPlan {
+  int64_t N, H, V;
+  int dtype, gw_dtype, esize;
+  bool accum_gw;                 // FLCE_ACCUMULATE_GRAD_WEIGHT
+  bool gw_acc32;                 // grad_weight summed over blocks in an fp32 workspace accumulator
+  int64_t n_ht, n_vt, V_pad;
+  int64_t rows_c;                // rows per block (multiple of 256)
+  int n_chunks;
+  int64_t Vc;                    // vocabulary chunk of the grad_inputs contraction
+  int n_vchunks;
+  size_t b_L, b_xt, b_giacc, b_gwacc, b_ghpart, b_bytes;
+};
+
+int make_chunk_plan(const flce_chunked_params* p, ChunkPlan* plan);
+int launch_chunked(const ChunkPlan& pl, const void* inputs, const void* weight, flce_chunk_loss_fn fn, void* user,
+                   float* loss, void* grad_inputs, void* grad_weight, char* ws, hipStream_t st);
+int launch_wmse(const flce_wmse_args& a, int64_t row0, int rows, int V, void* L, int ld, int dtype, float* loss,
+                hipStream_t st);
 
 hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
                           const void* targets, float* loss, float* lse, int64_t* num_correct,

@@ -168,3 +168,26 @@ def make_workload_inputs(wl: Workload) -> dict:
                        targets=wl.targets, zipf_s=wl.zipf_s,
                        ignore_frac=wl.ignore_frac, reduction=wl.reduction,
                        seed=wl.seed)
+
+
+def make_wmse_inputs(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
+                     weight_std: float = 0.02, hidden_std: float = 1.0, seed: int = 0) -> dict:
+    """Inputs of the weighted squared error through the generic chunked loss:
+    hidden (N,H) and weight (V,H) as in ``make_inputs``; target (N,V) float32
+    N(0,1); row_weight (N,) and feature_weight (V,) float32 uniform in [0.5, 1.5)."""
+    ss = np.random.SeedSequence(seed)
+    s_h, s_w, s_y, s_r, s_f = ss.spawn(5)
+    target = np.empty((n_tokens, vocab), dtype=np.float32)
+    flat = target.reshape(-1)
+    g = np.random.Generator(np.random.PCG64(s_y))
+    step = 1 << 24
+    for s0 in range(0, flat.size, step):
+        k = min(step, flat.size - s0)
+        flat[s0:s0 + k] = g.standard_normal(k, dtype=np.float32)
+    return {
+        "hidden": _normal(np.random.Generator(np.random.PCG64(s_h)), (n_tokens, hidden), hidden_std, dtype),
+        "weight": _normal(np.random.Generator(np.random.PCG64(s_w)), (vocab, hidden), weight_std, dtype),
+        "target": target,
+        "row_weight": np.random.Generator(np.random.PCG64(s_r)).uniform(0.5, 1.5, n_tokens).astype(np.float32),
+        "feature_weight": np.random.Generator(np.random.PCG64(s_f)).uniform(0.5, 1.5, vocab).astype(np.float32),
+    }

@@ -115,3 +115,40 @@ def test_null_and_misaligned_pointers_rejected(lib):
 def test_too_large_problem_rejected(lib):
     p = flce.make_params(1 << 20, 4096, 1000)       # N*H*2 bytes >= 2 GiB
     assert _ws(p, flce.FLCE_PASS_FORWARD)[0] == flce.FLCE_ERR_UNSUPPORTED
+
+
+def test_chunked_params_layout_and_validation(lib):
+    # 4 x int64, 4 x int32
+    assert ctypes.sizeof(flce.flce_chunked_params) == 48
+    assert ctypes.sizeof(flce.flce_wmse_args) == 40
+
+    def ws(p):
+        out = ctypes.c_size_t(0)
+        return lib.flce_chunked_workspace_size(ctypes.byref(p), ctypes.byref(out)), out.value
+
+    p = flce.make_chunked_params(8192, 4096, 128256, dtype="bf16")
+    rc, b = ws(p)
+    # one 4096-row block of bf16 logits (1.05 GB) + the fp32 grad_weight accumulator (2.1 GB)
+    assert rc == 0 and 3.0e9 < b < 3.3e9
+    p = flce.make_chunked_params(8192, 4096, 128256, dtype="bf16", grad_weight_accum_dtype="weight")
+    rc, b2 = ws(p)
+    assert rc == 0 and b2 < b - 2e9          # "weight" accumulation needs no fp32 accumulator
+    for field, value, code in (("chunk_rows", 100, flce.FLCE_ERR_UNSUPPORTED),
+                               ("chunk_rows", -256, flce.FLCE_ERR_INVALID_ARG),
+                               ("accum_dtype", flce.FLCE_F16, flce.FLCE_ERR_INVALID_ARG),
+                               ("flags", 2, flce.FLCE_ERR_INVALID_ARG),
+                               ("dtype", 5, flce.FLCE_ERR_INVALID_ARG),
+                               ("hidden", 12, flce.FLCE_ERR_UNSUPPORTED)):
+        q = flce.make_chunked_params(512, 64, 1000)
+        setattr(q, field, value)
+        assert ws(q)[0] == code, field
+    # missing loss function / loss pointer: rejected before any launch
+    q = flce.make_chunked_params(512, 64, 1000)
+    null_fn = ctypes.cast(None, flce.CHUNK_LOSS_FN)
+    assert lib.flce_chunked_linear_loss(ctypes.byref(q), 16, 16, null_fn, None, 16, 16, 16, 16, 1 << 30,
+                                        None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_chunked_linear_loss(ctypes.byref(q), 16, 16, flce.weighted_mse_chunk_fn(), None, None, 16, 16,
+                                        16, 1 << 30, None) == flce.FLCE_ERR_INVALID_ARG
+    # the built-in loss function checks its arguments on the host
+    assert lib.flce_weighted_mse_chunk(None, 0, 1, 10, 16, 16, 1, 16, None) == flce.FLCE_ERR_INVALID_ARG
+    assert flce.flce_status_string(flce.FLCE_ERR_CALLBACK) == "the chunk loss function reported an error"
