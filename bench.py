@@ -116,7 +116,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS))
+    ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS) + sorted(si.WMSE_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -131,6 +131,8 @@ def main():
     import linear_cross_entropy_tiled_amd as flce
 
     flce.load()
+    if args.workload in si.WMSE_WORKLOADS:
+        return run_wmse(args, torch, flce)
     wl = si.WORKLOADS[args.workload]
     inp = si.make_workload_inputs(wl)
     d = _to_dev(inp, wl.dtype)
@@ -232,6 +234,97 @@ def main():
         del d
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(inp, wl, min(args.cpu_rows, n))
+    print(json.dumps(out), flush=True)
+
+
+def run_wmse(args, torch, flce):
+    """One step = one flce_chunked_linear_loss call with the built-in weighted
+    squared error: block logits (2NHV), the loss kernel, grad_inputs (2NHV)
+    and grad_weight (2NHV); 6NHV flop."""
+    import ctypes
+    name = args.workload
+    n, h, v, dtype, wstd, seed = si.WMSE_WORKLOADS[name]
+    inp = si.make_wmse_inputs(n, h, v, dtype=dtype, weight_std=wstd, seed=seed)
+    d = _to_dev({k: inp[k] for k in ("hidden", "weight")} | {"bias": None, "targets": np.zeros(1, np.int64),
+                                                           "grad_loss": np.float32(1.0)}, dtype)
+    y = torch.from_numpy(inp["target"]).cuda()
+    r = torch.from_numpy(inp["row_weight"]).cuda()
+    f = torch.from_numpy(inp["feature_weight"]).cuda()
+    p = flce.make_chunked_params(n, h, v, dtype=dtype)
+    ws = torch.empty(flce.flce_chunked_workspace_size(p), dtype=torch.uint8, device="cuda")
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    gi = torch.empty((n, h), dtype=tdt[dtype], device="cuda")
+    gw = torch.empty((v, h), dtype=tdt[dtype], device="cuda")
+    row_loss = torch.empty(n, dtype=torch.float32, device="cuda")
+    a = flce.flce_wmse_args(y.data_ptr(), y.stride(0), r.data_ptr(), f.data_ptr(), row_loss.data_ptr())
+    user = ctypes.cast(ctypes.pointer(a), ctypes.c_void_p)
+    fn = flce.weighted_mse_chunk_fn()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rc = flce.flce_chunked_linear_loss(p, d["hidden"].data_ptr(), d["weight"].data_ptr(), fn, user,
+                                           loss.data_ptr(), gi.data_ptr(), gw.data_ptr(), ws.data_ptr(),
+                                           ws.numel(), stream.cuda_stream)
+        if rc:
+            raise flce.FlceError(rc, "flce_chunked_linear_loss")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = wall / args.steps * 1e3
+    ev_ms = float(np.mean([x.elapsed_time(z) for x, z in ev]))
+    tflops = 6.0 * n * h * v / (step_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if dtype in ("bf16", "f16") else PEAK_F32_TFLOPS
+    out = {
+        "metric": "generic chunked linear loss (weighted squared error) tokens/s and TFLOP/s (6NHV)",
+        "value": n / (step_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "n_tokens": n, "hidden": h, "vocab": v, "loss": "weighted squared error",
+                   "rows_per_block": int(p.chunk_rows) or "library choice", "grad_weight_accum_dtype": "fp32"},
+        "tflops": tflops,
+        "frac_of_peak": tflops / peak,
+        "event_ms_per_step": ev_ms,
+        "peak_mem_gib": torch.cuda.max_memory_allocated() / 2**30,
+        "device": _device_info(torch),
+        "roofline": {"bound": "mfma", "kernel": "whole step (block logits + two contractions, 6NHV)",
+                     "achieved": 6.0 * n * h * v / (ev_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
+                     "frac": 6.0 * n * h * v / (ev_ms * 1e-3) / 1e12 / peak, "traffic": None},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = min(args.cpu_rows, n) // 4
+        x = si.widen(inp["hidden"][:rows], dtype)
+        w = si.widen(inp["weight"], dtype)
+        t1 = time.perf_counter()
+        oracle.weighted_mse(x, w, inp["target"][:rows].astype(np.float64),
+                            inp["row_weight"][:rows].astype(np.float64), inp["feature_weight"].astype(np.float64))
+        dt = time.perf_counter() - t1
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count()
+        out["cpu_baseline"] = {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                               "sample": f"fp64 oracle weighted squared error of the first {rows} of {n} tokens "
+                                         f"against the full {v}-row weight ({dt:.1f} s)", "seconds": dt}
     print(json.dumps(out), flush=True)
 
 

@@ -191,3 +191,10 @@ def make_wmse_inputs(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf
         "row_weight": np.random.Generator(np.random.PCG64(s_r)).uniform(0.5, 1.5, n_tokens).astype(np.float32),
         "feature_weight": np.random.Generator(np.random.PCG64(s_f)).uniform(0.5, 1.5, vocab).astype(np.float32),
     }
+
+
+# The weighted squared error through the generic chunked loss at the headline
+# projection shape (N=8192, H=4096, V=128256): (n_tokens, hidden, vocab, dtype, weight_std, seed).
+WMSE_WORKLOADS = {
+    "wmse_bf16_n8192_h4096_v128256": (8192, 4096, 128256, "bf16", 0.02, 6),
+}
