@@ -117,6 +117,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS) + sorted(si.WMSE_WORKLOADS))
+    ap.add_argument("--path", choices=("split", "fused"), default="split",
+                    help="split: flce_forward then flce_backward (the backward recomputes the logit tiles); "
+                         "fused: flce_forward_backward (one pass, gradients from each row block's stored logits)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -133,6 +136,8 @@ def main():
     flce.load()
     if args.workload in si.WMSE_WORKLOADS:
         return run_wmse(args, torch, flce)
+    if args.path == "fused":
+        return run_fused(args, torch, flce)
     wl = si.WORKLOADS[args.workload]
     inp = si.make_workload_inputs(wl)
     d = _to_dev(inp, wl.dtype)
@@ -234,6 +239,81 @@ def main():
         del d
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(inp, wl, min(args.cpu_rows, n))
+    print(json.dumps(out), flush=True)
+
+
+def run_fused(args, torch, flce):
+    """One step = one flce_forward_backward call: per block of rows, the logit
+    tiles (2 x rows x H x V, stored in the input dtype), the logit gradient in
+    place, grad_hidden and grad_weight (2 x rows x H x V each): 6NHV flop
+    executed.  TFLOP/s is also given on the metric's 8NHV count."""
+    wl = si.WORKLOADS[args.workload]
+    inp = si.make_workload_inputs(wl)
+    d = _to_dev(inp, wl.dtype)
+    n, h, v = wl.n_tokens, wl.hidden, wl.vocab
+    opts = dict(logit_scale=wl.logit_scale, softcap=wl.softcap, z_loss=wl.z_loss,
+                ignore_index=si.IGNORE_INDEX, reduction=wl.reduction)
+    pf = flce.make_params(n, h, v, dtype=wl.dtype, grad_weight_dtype=wl.grad_weight_dtype, **opts)
+    ws = torch.empty(flce.flce_forward_backward_workspace_size(pf, 0), dtype=torch.uint8, device="cuda")
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+    loss = torch.empty(n if wl.reduction == "none" else 1, dtype=torch.float32, device="cuda")
+    lse = torch.empty(n, dtype=torch.float32, device="cuda")
+    nc = torch.empty(1, dtype=torch.int64, device="cuda")
+    ent = torch.empty(1, dtype=torch.float32, device="cuda")
+    gh = torch.empty((n, h), dtype=tdt[wl.dtype], device="cuda")
+    gw = torch.empty((v, h), dtype=tdt[wl.grad_weight_dtype or wl.dtype], device="cuda")
+    gb = torch.empty(v, dtype=tdt[wl.dtype], device="cuda") if d["bias"] is not None else None
+    gl = d["grad_loss"] if wl.reduction == "none" else d["grad_loss"][:1]
+    P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rc = flce.flce_forward_backward(pf, 0, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]), P(gl),
+                                        P(loss), P(lse), P(nc), P(ent), P(gh), P(gw), P(gb), P(ws), ws.numel(),
+                                        stream.cuda_stream)
+        if rc:
+            raise flce.FlceError(rc, "flce_forward_backward")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = wall / args.steps * 1e3
+    ev_ms = float(np.mean([x.elapsed_time(z) for x, z in ev]))
+    peak = PEAK_BF16_TFLOPS if wl.dtype in ("bf16", "f16") else PEAK_F32_TFLOPS
+    out = {
+        "metric": METRIC,
+        "value": n / (step_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "path": "fused (flce_forward_backward)", "n_tokens": n, "hidden": h,
+                   "vocab": v, "bias": wl.bias_std is not None, "logit_scale": wl.logit_scale,
+                   "softcap": wl.softcap, "z_loss": wl.z_loss, "ignore_frac": wl.ignore_frac,
+                   "reduction": wl.reduction, "grad_weight_dtype": wl.grad_weight_dtype or wl.dtype},
+        "tflops_8nhv": 8.0 * n * h * v / (step_ms * 1e-3) / 1e12,
+        "frac_of_peak_8nhv": 8.0 * n * h * v / (step_ms * 1e-3) / 1e12 / peak,
+        "tflops_executed_6nhv": 6.0 * n * h * v / (step_ms * 1e-3) / 1e12,
+        "frac_of_peak_executed": 6.0 * n * h * v / (step_ms * 1e-3) / 1e12 / peak,
+        "event_ms_per_step": ev_ms,
+        "peak_mem_gib": torch.cuda.max_memory_allocated() / 2**30,
+        "device": _device_info(torch),
+        "kernel_source_hash": kernel_source_hash(),
+    }
     print(json.dumps(out), flush=True)
 
 

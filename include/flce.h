@@ -140,9 +140,41 @@ int flce_backward(const flce_params* p, const void* hidden, const void* weight, 
                   void* grad_hidden, void* grad_weight, void* grad_bias, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * One-pass forward + backward (the row-chunked schedule of the "Chunked Linear
+ * Cross-Entropy" page, "Kernel design", and of quack-kernels'
+ * chunked_linear_cross_entropy: the gradients are formed while the logits of a
+ * block of rows exist, instead of recomputing them in a later backward call).
+ * For callers that know the upstream gradient before the forward pass (the
+ * loss is the last node: grad_loss = 1, or a loss scale).
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of device workspace flce_forward_backward needs.  block_rows: rows per
+ * block, a multiple of 256, or 0 for the library's choice (the most rows whose
+ * logits, block_rows x V in the input dtype, fit in 1 GiB).  Host only. */
+int flce_forward_backward_workspace_size(const flce_params* p, int64_t block_rows, size_t* bytes);
+
 /*
- * Synchronises `stream`, then reads the status word that the last forward or
- * backward call on this workspace left: FLCE_OK, FLCE_ERR_TARGET_OUT_OF_RANGE,
+ * The outputs of flce_forward followed by flce_backward with the same
+ * grad_loss, in one call: loss, lse, num_correct, entropy_sum (as flce_forward)
+ * and grad_hidden, grad_weight, grad_bias (as flce_backward; grad_loss is a
+ * device fp32 scalar for sum / mean, N values for none).  Per block of rows the
+ * logit tiles are computed once and written to the workspace in the input
+ * dtype; loss, LSE and metrics come from their fp32 values, the logit gradient
+ * from the stored ones (as the pages' chunked paths keep logits in the logits
+ * dtype), so results agree with the two-call path to rounding, not bitwise.
+ * grad_weight is summed over the blocks in fp32 and rounded once.  Costs
+ * 3 x 2NHV flop instead of 4 x 2NHV.  Argument rules, flags and status codes
+ * are those of flce_forward and flce_backward.
+ */
+int flce_forward_backward(const flce_params* p, int64_t block_rows, const void* hidden, const void* weight,
+                          const void* bias, const void* targets, const float* grad_loss, float* loss, float* lse,
+                          int64_t* num_correct, float* entropy_sum, void* grad_hidden, void* grad_weight,
+                          void* grad_bias, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Synchronises `stream`, then reads the status word that the last forward,
+ * backward or forward-backward call on this workspace left: FLCE_OK, FLCE_ERR_TARGET_OUT_OF_RANGE,
  * or FLCE_ERR_HIP if the stream reports an error.
  */
 int flce_get_status(const void* workspace, void* stream);

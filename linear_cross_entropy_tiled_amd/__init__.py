@@ -45,7 +45,8 @@ FLCE_TARGETS_INT32 = 4
 
 EXPORTED = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_get_status",
             "flce_status_string", "flce_version", "flce_chunked_workspace_size",
-            "flce_chunked_linear_loss", "flce_weighted_mse_chunk")
+            "flce_chunked_linear_loss", "flce_weighted_mse_chunk", "flce_forward_backward_workspace_size",
+            "flce_forward_backward")
 
 
 class flce_params(ctypes.Structure):
@@ -109,6 +110,10 @@ def load(path: Optional[str] = None):
     if _lib is not None:
         return _lib
     path = path or LIB_PATH
+    # torch first: the library links the HIP runtime by soname, and the copy
+    # torch ships must be the one in the process (a second runtime loaded
+    # ahead of torch's crashes it)
+    import torch  # noqa: F401
     if not os.path.exists(path):
         raise FileNotFoundError(
             f"{path} is missing: build it with `python -m linear_cross_entropy_tiled_amd.build`")
@@ -127,6 +132,11 @@ def load(path: Optional[str] = None):
     lib.flce_status_string.restype = ctypes.c_char_p
     lib.flce_version.argtypes = []
     lib.flce_version.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.flce_forward_backward_workspace_size.argtypes = [P, i64, ctypes.POINTER(sz)]
+    lib.flce_forward_backward_workspace_size.restype = ctypes.c_int
+    lib.flce_forward_backward.argtypes = [P, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.flce_forward_backward.restype = ctypes.c_int
     CP = ctypes.POINTER(flce_chunked_params)
     lib.flce_chunked_workspace_size.argtypes = [CP, ctypes.POINTER(sz)]
     lib.flce_chunked_workspace_size.restype = ctypes.c_int
@@ -160,6 +170,22 @@ def flce_backward(params, hidden, weight, bias, targets, lse, grad_loss, grad_hi
     return load().flce_backward(ctypes.byref(params), hidden, weight, bias, targets, lse, grad_loss,
                                 grad_hidden, grad_weight, grad_bias, workspace, workspace_bytes,
                                 stream)
+
+
+def flce_forward_backward_workspace_size(params: flce_params, block_rows: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    rc = load().flce_forward_backward_workspace_size(ctypes.byref(params), block_rows, ctypes.byref(out))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_forward_backward_workspace_size")
+    return out.value
+
+
+def flce_forward_backward(params, block_rows, hidden, weight, bias, targets, grad_loss, loss, lse, num_correct,
+                          entropy_sum, grad_hidden, grad_weight, grad_bias, workspace, workspace_bytes,
+                          stream) -> int:
+    return load().flce_forward_backward(ctypes.byref(params), block_rows, hidden, weight, bias, targets, grad_loss,
+                                        loss, lse, num_correct, entropy_sum, grad_hidden, grad_weight, grad_bias,
+                                        workspace, workspace_bytes, stream)
 
 
 def flce_chunked_workspace_size(params: flce_chunked_params) -> int:
@@ -327,6 +353,54 @@ def backward(hidden, weight, targets, lse, grad_loss, bias=None, *, logit_scale:
     if rc != FLCE_OK:
         raise FlceError(rc, "flce_backward")
     return gh, gw, gb
+
+
+def forward_backward(hidden, weight, targets, grad_loss, bias=None, *, logit_scale: float = 1.0,
+                     softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
+                     reduction: str = "mean", grad_weight_dtype: Optional[str] = None, return_metrics: bool = False,
+                     block_rows: int = 0, workspace=None, grad_weight=None, grad_bias=None):
+    """Runs flce_forward_backward (loss and gradients in one pass, the upstream gradient
+    ``grad_loss`` given up front) on the current stream.  Returns
+    (loss, lse, metrics | None, grad_hidden, grad_weight, grad_bias); ``grad_weight`` /
+    ``grad_bias`` given: accumulated into in place, as in ``backward``."""
+    import torch
+    for t, n in ((hidden, "hidden"), (weight, "weight"), (targets, "targets"), (bias, "bias"),
+                 (grad_loss, "grad_loss"), (grad_weight, "grad_weight"), (grad_bias, "grad_bias")):
+        _check(t, n)
+    n, h = hidden.shape
+    v = weight.shape[0]
+    dt = _dtype_name(hidden)
+    if grad_weight is not None:
+        grad_weight_dtype = _dtype_name(grad_weight)
+        if tuple(grad_weight.shape) != (v, h):
+            raise ValueError("grad_weight must have the weight's shape")
+    if grad_bias is not None and (bias is None or grad_bias.dtype != bias.dtype or grad_bias.numel() != v):
+        raise ValueError("grad_bias must match bias")
+    p = make_params(n, h, v, dtype=dt, grad_weight_dtype=grad_weight_dtype, logit_scale=logit_scale,
+                    softcap=softcap, z_loss=z_loss, ignore_index=ignore_index, reduction=reduction,
+                    accumulate_grad_weight=grad_weight is not None, accumulate_grad_bias=grad_bias is not None,
+                    targets_int32=_targets_int32(targets))
+    dev = hidden.device
+    ws_bytes = flce_forward_backward_workspace_size(p, block_rows)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+    loss = torch.empty(n if reduction == "none" else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    nc = torch.empty(1, dtype=torch.int64, device=dev) if return_metrics else None
+    ent = torch.empty(1, dtype=torch.float32, device=dev) if return_metrics else None
+    gh = torch.empty((n, h), dtype=hidden.dtype, device=dev)
+    gw = grad_weight if grad_weight is not None else torch.empty((v, h), dtype=tdt[grad_weight_dtype or dt], device=dev)
+    gb = grad_bias if grad_bias is not None else (torch.empty(v, dtype=bias.dtype, device=dev) if bias is not None else None)
+    rc = flce_forward_backward(p, block_rows, _ptr(hidden), _ptr(weight), _ptr(bias), _ptr(targets), _ptr(grad_loss),
+                               _ptr(loss), _ptr(lse), _ptr(nc), _ptr(ent), _ptr(gh), _ptr(gw), _ptr(gb),
+                               _ptr(workspace), workspace.numel(), _stream_handle(dev))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_forward_backward")
+    if reduction != "none":
+        loss = loss.reshape(())
+    metrics = {"num_correct_tokens": nc.reshape(()), "entropy_sum": ent.reshape(())} if return_metrics else None
+    return loss, lse, metrics, gh, gw, gb
 
 
 def get_status(workspace) -> int:

@@ -32,6 +32,13 @@ void plan_gh_split(int64_t tiles, int64_t cvn, int esize, int64_t N, int64_t H, 
   *parts_out = (int)((stages + kt - 1) / kt);
 }
 
+int forward_splits(int64_t n_tt, int64_t n_vt) {
+  int64_t S = n_tt > 0 ? (kTargetWorkgroups + n_tt / 2) / n_tt : 1;
+  if (S < 1) S = 1;
+  if (S > n_vt) S = n_vt;
+  return (int)S;
+}
+
 int make_plan(const flce_params* p, Plan* pl) {
   if (!p || !pl) return FLCE_ERR_INVALID_ARG;
   if (p->n_tokens < 0 || p->hidden <= 0 || p->vocab <= 0) return FLCE_ERR_INVALID_ARG;
@@ -76,9 +83,7 @@ int make_plan(const flce_params* p, Plan* pl) {
   P.V_pad = P.n_vt * 256;
 
   // forward: split the vocabulary so that about one workgroup runs per CU
-  int64_t S = P.n_tt > 0 ? (kTargetWorkgroups + P.n_tt / 2) / P.n_tt : 1;
-  if (S < 1) S = 1;
-  if (S > P.n_vt) S = P.n_vt;
+  const int64_t S = forward_splits(P.n_tt, P.n_vt);
   P.S = (int)S;
   P.f_part = kStatusBytes;
   const size_t part_bytes = size_t(5) * S * P.N_pad * 4;
@@ -202,6 +207,72 @@ int make_chunk_plan(const flce_chunked_params* p, ChunkPlan* pl) {
   return FLCE_OK;
 }
 
+// One-pass forward + backward: blocks of rows whose logits (rows x V_pad in the
+// input dtype) fit the logits budget.
+int plan_forward_backward(Plan* pl, int64_t block_rows) {
+  Plan& P = *pl;
+  if (block_rows < 0 || block_rows % 256 != 0) return FLCE_ERR_UNSUPPORTED;
+  const int64_t row_bytes = P.V_pad * P.esize;
+  int64_t rows = block_rows;
+  if (rows == 0) {
+    rows = (int64_t)(kLogitsBlockBudget / (size_t)row_bytes) / 256 * 256;
+    if (rows > P.N_pad) rows = P.N_pad;
+    if (rows < 256) rows = 256;
+  }
+  if (rows * row_bytes >= (int64_t(1) << 31) || rows * P.H * P.esize >= (int64_t(1) << 31))
+    return FLCE_ERR_UNSUPPORTED;
+  P.fb_rows = rows;
+  P.fb_blocks = P.N > 0 ? (int)((P.N + rows - 1) / rows) : 0;
+  int64_t vc = ((int64_t(1) << 31) - 1) / (P.H * P.esize) / 256 * 256;
+  if (vc < 256) return FLCE_ERR_UNSUPPORTED;
+  if (vc > P.V_pad) vc = P.V_pad;
+  P.fb_Vc = vc;
+  P.fb_vchunks = (int)((P.V_pad + vc - 1) / vc);
+  P.fb_gw_acc32 = P.gw_dtype != FLCE_F32 && P.fb_blocks > 1;
+  const int64_t last = P.N > 0 ? P.N - (int64_t)(P.fb_blocks - 1) * rows : 0;
+  const int64_t full_tt = rows / 256, last_tt = (last + 255) / 256;
+
+  size_t o = kStatusBytes;
+  P.fb_part = o;
+  {
+    const size_t a = size_t(forward_splits(full_tt, P.n_vt)) * rows;
+    const size_t b = size_t(forward_splits(last_tt, P.n_vt)) * last_tt * 256;
+    o = align_up(o + 5 * 4 * (a > b ? a : b), 256);
+  }
+  P.fb_blk = o;
+  o = align_up(o + size_t(P.n_tt > 0 ? P.n_tt : 1) * sizeof(BlockPart), 256);
+  P.fb_coefA = o;
+  o = align_up(o + size_t(P.N_pad) * 4, 256);
+  P.fb_coefB = o;
+  o = align_up(o + size_t(P.N_pad) * 4, 256);
+  P.fb_lseL = o;
+  o = align_up(o + size_t(P.N_pad) * 4, 256);
+  P.fb_tgt = o;
+  o = align_up(o + size_t(P.N_pad) * 4, 256);
+  P.fb_Z = o;
+  o = align_up(o + size_t(rows) * row_bytes, 256);
+  P.fb_xt = o;
+  o = align_up(o + size_t(P.H) * rows * P.esize, 256);
+  P.fb_ghacc = o;
+  if (P.dtype != FLCE_F32 && P.fb_vchunks > 1) o = align_up(o + size_t(rows) * P.H * 4, 256);
+  P.fb_gwacc = o;
+  if (P.fb_gw_acc32) o = align_up(o + size_t(P.V) * P.H * 4, 256);
+  P.fb_ghpart = o;
+  {
+    int parts = 1, kt = 0, parts2 = 1;
+    plan_gh_split(P.n_ht * full_tt, vc, P.esize, rows, P.H, &parts, &kt);
+    plan_gh_split(P.n_ht * last_tt, vc, P.esize, last, P.H, &parts2, &kt);
+    size_t part_bytes = 0;
+    if (parts > 1) part_bytes = size_t(parts) * rows * P.H * 4;
+    if (parts2 > 1 && size_t(parts2) * last * P.H * 4 > part_bytes) part_bytes = size_t(parts2) * last * P.H * 4;
+    o = align_up(o + part_bytes, 256);
+  }
+  P.fb_gbpart = o;
+  o = align_up(o + size_t(P.N_pad) / 256 * P.V_pad * 4, 256);
+  P.fb_bytes = o;
+  return FLCE_OK;
+}
+
 }  // namespace flce
 
 using namespace flce;
@@ -273,6 +344,42 @@ int flce_backward(const flce_params* p, const void* hidden, const void* weight, 
   hipError_t e = launch_backward(pl, hidden, weight, bias, targets, lse, grad_loss, grad_hidden,
                                  grad_weight, grad_bias, static_cast<char*>(workspace),
                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+int flce_forward_backward_workspace_size(const flce_params* p, int64_t block_rows, size_t* bytes) {
+  if (!bytes) return FLCE_ERR_INVALID_ARG;
+  Plan pl;
+  int rc = make_plan(p, &pl);
+  if (rc != FLCE_OK) return rc;
+  rc = plan_forward_backward(&pl, block_rows);
+  if (rc != FLCE_OK) return rc;
+  *bytes = pl.fb_bytes;
+  return FLCE_OK;
+}
+
+int flce_forward_backward(const flce_params* p, int64_t block_rows, const void* hidden, const void* weight,
+                          const void* bias, const void* targets, const float* grad_loss, float* loss, float* lse,
+                          int64_t* num_correct, float* entropy_sum, void* grad_hidden, void* grad_weight,
+                          void* grad_bias, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  int rc = make_plan(p, &pl);
+  if (rc != FLCE_OK) return rc;
+  rc = plan_forward_backward(&pl, block_rows);
+  if (rc != FLCE_OK) return rc;
+  pl.has_bias = bias != nullptr;
+  if (!weight || !grad_weight || !workspace) return FLCE_ERR_INVALID_ARG;
+  if (!loss && (pl.reduction != FLCE_REDUCTION_NONE || pl.N > 0)) return FLCE_ERR_INVALID_ARG;
+  if (!grad_loss && (pl.reduction != FLCE_REDUCTION_NONE || pl.N > 0)) return FLCE_ERR_INVALID_ARG;
+  if (pl.N > 0 && (!hidden || !targets || !lse || !grad_hidden)) return FLCE_ERR_INVALID_ARG;
+  if (grad_bias && !bias) return FLCE_ERR_INVALID_ARG;
+  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(bias) || !aligned16(workspace) ||
+      !aligned16(targets) || !aligned16(grad_hidden) || !aligned16(grad_weight) || !aligned16(grad_bias))
+    return FLCE_ERR_UNSUPPORTED;
+  if (workspace_bytes < pl.fb_bytes) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  hipError_t e = launch_forward_backward(pl, hidden, weight, bias, targets, grad_loss, loss, lse, num_correct,
+                                         entropy_sum, grad_hidden, grad_weight, grad_bias,
+                                         static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 

@@ -46,6 +46,7 @@ struct PrepArgs {
   float* dscale;  // [0] = 2^s, [1] = 2^-s (see above)
   int f16_d;      // dlogits are fp16: choose s; else s = 0
   float abs_scale;
+  int row0, row1; // coefficients (and the fp16 bound) for rows [row0, row1) only; n_valid counts all N
 };
 
 __global__ __launch_bounds__(1024) void bwd_prep_kernel(PrepArgs a) {
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(PrepArgs a) {
   const float g0 = a.reduction == FLCE_REDUCTION_NONE ? 0.0f : a.grad_loss[0];
   const float c_all = a.reduction == FLCE_REDUCTION_SUM ? g0 : (n_valid > 0 ? g0 / (float)n_valid : 0.0f);
   float dmax = 0.0f;
-  for (int i = tid; i < a.N_pad; i += 1024) {
+  for (int i = a.row0 + tid; i < a.row1; i += 1024) {
     float ca = 0.0f, cb = 0.0f, ll = 0.0f;
     int tg = -1;
     if (i < a.N) {
@@ -553,18 +554,11 @@ __global__ __launch_bounds__(256) void bwd_gb_reduce(const float* part, int n_tt
   gb[v] = (T)s;
 }
 
-template <typename T>
-static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const void* weight,
-                                    const void* bias, const void* targets, const float* lse,
-                                    const float* grad_loss, void* grad_hidden, void* grad_weight,
-                                    void* grad_bias, char* ws, hipStream_t st) {
-  float* coefA = reinterpret_cast<float*>(ws + pl.b_coefA);
-  float* coefB = reinterpret_cast<float*>(ws + pl.b_coefB);
-  float* lseL = reinterpret_cast<float*>(ws + pl.b_lseL);
-  int* tgt = reinterpret_cast<int*>(ws + pl.b_tgt);
-  char* D = ws + pl.b_D;
-  float* gb_part = reinterpret_cast<float*>(ws + pl.b_gbpart);
-
+// Per-row coefficients of rows [row0, row1) (n_valid over all rows) and the
+// fp16 dlogits factor from those rows.
+void launch_prep_rows(const Plan& pl, const void* targets, const float* lse, const float* grad_loss, float* coefA,
+                      float* coefB, float* lseL, int* tgt, int* status, float* dscale, int64_t row0, int64_t row1,
+                      hipStream_t st) {
   PrepArgs pa;
   pa.targets = targets;
   pa.tgt_i32 = pl.tgt_i32 ? 1 : 0;
@@ -580,12 +574,30 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
   pa.coefB = coefB;
   pa.lseL = lseL;
   pa.tgt = tgt;
-  pa.status = reinterpret_cast<int*>(ws);
-  float* dscale = reinterpret_cast<float*>(ws + kDscaleOffset);
+  pa.status = status;
   pa.dscale = dscale;
   pa.f16_d = pl.dtype == FLCE_F16;
   pa.abs_scale = fabsf(pl.scale);
+  pa.row0 = (int)row0;
+  pa.row1 = (int)row1;
   bwd_prep_kernel<<<1, 1024, 0, st>>>(pa);
+}
+
+template <typename T>
+static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const void* weight,
+                                    const void* bias, const void* targets, const float* lse,
+                                    const float* grad_loss, void* grad_hidden, void* grad_weight,
+                                    void* grad_bias, char* ws, hipStream_t st) {
+  float* coefA = reinterpret_cast<float*>(ws + pl.b_coefA);
+  float* coefB = reinterpret_cast<float*>(ws + pl.b_coefB);
+  float* lseL = reinterpret_cast<float*>(ws + pl.b_lseL);
+  int* tgt = reinterpret_cast<int*>(ws + pl.b_tgt);
+  char* D = ws + pl.b_D;
+  float* gb_part = reinterpret_cast<float*>(ws + pl.b_gbpart);
+
+  float* dscale = reinterpret_cast<float*>(ws + kDscaleOffset);
+  launch_prep_rows(pl, targets, lse, grad_loss, coefA, coefB, lseL, tgt, reinterpret_cast<int*>(ws), dscale, 0,
+                   pl.N_pad, st);
 
   T* hiddenT = reinterpret_cast<T*>(ws + pl.b_xt);
   if (pl.N > 0) launch_transpose_hidden(pl.dtype, hidden, (int)pl.N, (int)pl.H, (int)pl.N_pad, hiddenT, st);
@@ -679,6 +691,17 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
                                                                pl.accum_gb ? 1 : 0, dscale);
   }
   return hipGetLastError();
+}
+
+void launch_gb_reduce(int dtype, const float* part, int n_tt, int ld, int V, void* gb, int accumulate,
+                      const float* dscale, hipStream_t st) {
+  const int nwg = (V + 255) / 256;
+  if (dtype == FLCE_BF16)
+    bwd_gb_reduce<bf16><<<nwg, 256, 0, st>>>(part, n_tt, ld, V, reinterpret_cast<bf16*>(gb), accumulate, dscale);
+  else if (dtype == FLCE_F16)
+    bwd_gb_reduce<f16><<<nwg, 256, 0, st>>>(part, n_tt, ld, V, reinterpret_cast<f16*>(gb), accumulate, dscale);
+  else
+    bwd_gb_reduce<float><<<nwg, 256, 0, st>>>(part, n_tt, ld, V, reinterpret_cast<float*>(gb), accumulate, dscale);
 }
 
 template <typename T>

@@ -25,6 +25,8 @@ struct FwdTileArgs {
   float* part_T;
   int* part_idx;
   float* part_zt;
+  void* z;          // STORE_Z: logits of the tile rows, z[t - t_first][v], row stride ldz elements
+  int ldz;
 };
 
 // Per-lane running softmax state for one token column.
@@ -44,11 +46,45 @@ __device__ __forceinline__ void merge_state(RowState& a, const RowState& b) {
   a.zt = fmaxf(a.zt, b.zt);
 }
 
-template <typename T, bool HAS_BIAS, bool SOFTCAP>
+// Four consecutive logits of one token, rounded to the input type.
+__device__ __forceinline__ void store_z4(float* p, const float* z) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{z[0], z[1], z[2], z[3]};
+}
+__device__ __forceinline__ void store_z4(bf16* p, const float* z) {
+  bf16x4 v;
+#pragma unroll
+  for (int j = 0; j < 4; j++) v[j] = (bf16)z[j];
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store_z4(f16* p, const float* z) {
+  f16x4 v;
+#pragma unroll
+  for (int j = 0; j < 4; j++) v[j] = (f16)z[j];
+  *reinterpret_cast<f16x4*>(p) = v;
+}
+
+// STORE_Z: also write every transformed logit z of the tiles to a.z (the row
+// block's logits for the one-pass forward + backward); rows past V and tokens
+// past N get finite values that the logit-gradient pass overwrites.
+template <typename T, bool HAS_BIAS, bool SOFTCAP, bool STORE_Z>
 __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   constexpr int E = sizeof(T);
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int tt = L / a.S, s = L % a.S;
+  // Token tiles x splits.  With whole groups of 4 token tiles, splits in
+  // multiples of 8 and at least 256 workgroups, ids walk 4 token tiles, then
+  // the next split, so the 32 ids one XCD runs at once are 4 token tiles x 8
+  // splits: each hidden tile is read by 8 of them and each weight tile by 4,
+  // the least fabric traffic for 32 resident tiles.  Otherwise token-tile
+  // major: the 32 ids are 32/S token tiles x S splits.
+  const int n_tt = (int)gridDim.x / a.S;
+  const bool grouped = a.S % 8 == 0 && n_tt % 4 == 0 && gridDim.x >= 256;
+  int tt, s;
+  if (grouped) {
+    grouped_tile(L, n_tt, a.S, 4, tt, s);
+  } else {
+    tt = L / a.S;
+    s = L % a.S;
+  }
   const int vt_begin = (int)((int64_t)s * a.n_vt / a.S);
   const int vt_end = (int)((int64_t)(s + 1) * a.n_vt / a.S);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -78,17 +114,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   db.k_bytes = a.H * E;
   const int KT = (a.H * E + kBKB - 1) / kBKB;
 
-  // One XCD runs `win` consecutive ids at once: win/S token tiles x S splits.
-  // The S splits of a token tile share its hidden rows; the win/S token tiles
-  // of a split read the same weight tile at the same time.
+  // One XCD runs `win` consecutive ids at once.  The splits of a token tile
+  // share its hidden rows; the token tiles of a split read the same weight
+  // tile at the same time.
   const int win = min(32, max(1, (int)gridDim.x / 8));
   L2Share sh;
-  sh.b_n = min(a.S, win);
-  sh.b_rank = s % sh.b_n;
-  sh.a_n = a.S <= win ? win / a.S : 1;
-  sh.a_rank = tt % sh.a_n;
-  if (sh.a_n < 2) sh.a_n = 0;
-  if (sh.b_n < 2) sh.b_n = 0;
+  if (grouped) {
+    sh.a_n = 4;
+    sh.a_rank = tt & 3;
+    sh.b_n = 8;
+    sh.b_rank = s & 7;
+  } else {
+    sh.b_n = min(a.S, win);
+    sh.b_rank = s % sh.b_n;
+    sh.a_n = a.S <= win ? win / a.S : 1;
+    sh.a_rank = tt % sh.a_n;
+    if (sh.a_n < 2) sh.a_n = 0;
+    if (sh.b_n < 2) sh.b_n = 0;
+  }
 
   // the bias of each vocabulary tile is staged in LDS (two buffers, by tile
   // parity: a tile's bias is written only after every wave has passed the
@@ -149,6 +192,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
         for (int r = 0; r < 16; r++) {
           u[r] = HAS_BIAS ? fmaf(acc[mi][ni][r], s_u, sb[r]) : acc[mi][ni][r] * s_u;
           if constexpr (SOFTCAP) rr[r] = fast_rcp(fast_exp2(u[r]) + 1.0f);
+        }
+        if constexpr (STORE_Z) {
+          const int t = wn * kWaveN + ni * 32 + (lane & 31);   // within this token tile
+          T* zrow = reinterpret_cast<T*>(a.z) + (size_t)(t0 + t) * a.ldz + vw + mi * 32 + 4 * (lane >> 5);
+#pragma unroll
+          for (int g = 0; g < 4; g++) {
+            float z4[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) z4[j] = SOFTCAP ? fmaf(-a.two_cap, rr[4 * g + j], a.cap) : u[4 * g + j];
+            store_z4(zrow + 8 * g, z4);
+          }
         }
         if (ragged) {
 #pragma unroll
@@ -409,36 +463,47 @@ __global__ __launch_bounds__(256) void fwd_finalize_scalars(ScalarArgs a) {
   }
 }
 
-template <typename T>
-static void launch_fwd_tiles(const Plan& pl, const FwdTileArgs& args, int nwg, hipStream_t st) {
+template <typename T, bool STORE_Z>
+static void launch_fwd_tiles_z(const Plan& pl, const FwdTileArgs& args, int nwg, hipStream_t st) {
   if (pl.has_bias) {
-    if (pl.cap > 0) fwd_tiles_kernel<T, true, true><<<nwg, kThreads, 0, st>>>(args);
-    else fwd_tiles_kernel<T, true, false><<<nwg, kThreads, 0, st>>>(args);
+    if (pl.cap > 0) fwd_tiles_kernel<T, true, true, STORE_Z><<<nwg, kThreads, 0, st>>>(args);
+    else fwd_tiles_kernel<T, true, false, STORE_Z><<<nwg, kThreads, 0, st>>>(args);
   } else {
-    if (pl.cap > 0) fwd_tiles_kernel<T, false, true><<<nwg, kThreads, 0, st>>>(args);
-    else fwd_tiles_kernel<T, false, false><<<nwg, kThreads, 0, st>>>(args);
+    if (pl.cap > 0) fwd_tiles_kernel<T, false, true, STORE_Z><<<nwg, kThreads, 0, st>>>(args);
+    else fwd_tiles_kernel<T, false, false, STORE_Z><<<nwg, kThreads, 0, st>>>(args);
   }
 }
 
-hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
-                          const void* targets, float* loss, float* lse, int64_t* num_correct,
-                          float* entropy_sum, char* ws, hipStream_t st) {
-  const size_t NP = (size_t)pl.N_pad * pl.S;
-  float* part_m = reinterpret_cast<float*>(ws + pl.f_part);
+template <typename T>
+static void launch_fwd_tiles(const Plan& pl, const FwdTileArgs& args, int nwg, hipStream_t st) {
+  if (args.z) launch_fwd_tiles_z<T, true>(pl, args, nwg, st);
+  else launch_fwd_tiles_z<T, false>(pl, args, nwg, st);
+}
+
+// The tile kernel and the per-row merge for rows [r0, r0 + rows) of the batch:
+// S vocabulary splits, partials in part (5 arrays of S x rows_pad), one
+// BlockPart per 256 rows at blk[r0 / 256 ...], LSE (and the per-row loss for
+// "none") at row r0 onwards; z: optional logits buffer (row stride ldz).
+void launch_forward_rows(const Plan& pl, const void* hidden, const void* weight, const void* bias,
+                         const void* targets, int64_t r0, int rows, int S, float* part, float* loss, float* lse,
+                         BlockPart* blk, void* z, int ldz, hipStream_t st) {
+  const int n_tt = (rows + 255) / 256;
+  const int rows_pad = n_tt * 256;
+  const size_t NP = (size_t)rows_pad * S;
+  float* part_m = part;
   float* part_l = part_m + NP;
   float* part_T = part_l + NP;
   float* part_zt = part_T + NP;
   int* part_idx = reinterpret_cast<int*>(part_zt + NP);
-  BlockPart* blk = reinterpret_cast<BlockPart*>(ws + pl.f_blk);
-
-  if (pl.N > 0) {
+  const void* tg = static_cast<const char*>(targets) + (size_t)r0 * (pl.tgt_i32 ? 4 : 8);
+  if (rows > 0) {
     FwdTileArgs a;
-    a.hidden = static_cast<const char*>(hidden);
+    a.hidden = static_cast<const char*>(hidden) + (size_t)r0 * pl.H * pl.esize;
     a.weight = static_cast<const char*>(weight);
     a.bias = bias;
-    a.targets = targets;
+    a.targets = tg;
     a.tgt_i32 = pl.tgt_i32 ? 1 : 0;
-    a.N = (int)pl.N;
+    a.N = rows;
     a.H = (int)pl.H;
     a.V = (int)pl.V;
     a.ignore_index = pl.ignore_index;
@@ -447,26 +512,28 @@ hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight
     a.two_log2e_over_cap = pl.cap > 0 ? 2.0f * kLog2e / pl.cap : 0.0f;
     a.two_cap = 2.0f * pl.cap;
     a.n_vt = (int)pl.n_vt;
-    a.S = pl.S;
-    a.N_pad = (int)pl.N_pad;
+    a.S = S;
+    a.N_pad = rows_pad;
     a.part_m = part_m;
     a.part_l = part_l;
     a.part_T = part_T;
     a.part_idx = part_idx;
     a.part_zt = part_zt;
-    const int nwg = (int)(pl.n_tt * pl.S);
+    a.z = z;
+    a.ldz = ldz;
+    const int nwg = n_tt * S;
     if (pl.dtype == FLCE_BF16) launch_fwd_tiles<bf16>(pl, a, nwg, st);
     else if (pl.dtype == FLCE_F16) launch_fwd_tiles<f16>(pl, a, nwg, st);
     else launch_fwd_tiles<float>(pl, a, nwg, st);
   }
-  const int nblk = (int)((pl.N + 255) / 256) > 0 ? (int)((pl.N + 255) / 256) : 1;
+  const int nblk = n_tt > 0 ? n_tt : 1;
   FinArgs f;
-  f.targets = targets;
+  f.targets = tg;
   f.tgt_i32 = pl.tgt_i32 ? 1 : 0;
-  f.N = (int)pl.N;
+  f.N = rows;
   f.V = (int)pl.V;
-  f.S = pl.S;
-  f.N_pad = (int)pl.N_pad;
+  f.S = S;
+  f.N_pad = rows_pad;
   f.reduction = pl.reduction;
   f.ignore_index = pl.ignore_index;
   f.z_loss = pl.z_loss;
@@ -475,10 +542,15 @@ hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight
   f.part_T = part_T;
   f.part_idx = part_idx;
   f.part_zt = part_zt;
-  f.loss = loss;
-  f.lse = lse;
-  f.blk = blk;
+  f.loss = loss ? loss + r0 : nullptr;
+  f.lse = lse ? lse + r0 : nullptr;
+  f.blk = blk + r0 / 256;
   fwd_finalize_rows<<<nblk, 256, 0, st>>>(f);
+}
+
+// Fixed-order sums of the nblk BlockParts: the reduced loss, the metrics and the status word.
+void launch_forward_scalars(const Plan& pl, const BlockPart* blk, int nblk, float* loss, int64_t* num_correct,
+                            float* entropy_sum, int* status, hipStream_t st) {
   ScalarArgs sa;
   sa.blk = blk;
   sa.nblk = nblk;
@@ -486,8 +558,18 @@ hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight
   sa.loss = loss;
   sa.num_correct = num_correct;
   sa.entropy_sum = entropy_sum;
-  sa.status = reinterpret_cast<int*>(ws);
+  sa.status = status;
   fwd_finalize_scalars<<<1, 256, 0, st>>>(sa);
+}
+
+hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
+                          const void* targets, float* loss, float* lse, int64_t* num_correct,
+                          float* entropy_sum, char* ws, hipStream_t st) {
+  BlockPart* blk = reinterpret_cast<BlockPart*>(ws + pl.f_blk);
+  launch_forward_rows(pl, hidden, weight, bias, targets, 0, (int)pl.N, pl.S, reinterpret_cast<float*>(ws + pl.f_part),
+                      loss, lse, blk, nullptr, 0, st);
+  const int nblk = pl.N > 0 ? (int)pl.n_tt : 1;
+  launch_forward_scalars(pl, blk, nblk, loss, num_correct, entropy_sum, reinterpret_cast<int*>(ws), st);
   return hipGetLastError();
 }
 

@@ -32,12 +32,30 @@ struct Plan {
   int gh_parts;                  // grad_hidden: K (vocabulary) splits per chunk when there are few output tiles
   int gh_kt_per_part;            // 64-row stages per split
   size_t b_coefA, b_coefB, b_lseL, b_tgt, b_D, b_xt, b_ghacc, b_ghpart, b_gbpart, b_bytes;
+
+  // one-pass forward + backward (plan_forward_backward): blocks of fb_rows rows
+  int64_t fb_rows;               // rows per block, a multiple of 256
+  int fb_blocks;
+  int64_t fb_Vc;                 // vocabulary chunk of the grad_hidden contraction (32-bit weight offsets)
+  int fb_vchunks;
+  bool fb_gw_acc32;              // grad_weight summed over the blocks in an fp32 workspace accumulator
+  size_t fb_part, fb_blk, fb_coefA, fb_coefB, fb_lseL, fb_tgt, fb_Z, fb_xt, fb_ghacc, fb_gwacc, fb_ghpart,
+      fb_gbpart, fb_bytes;
 };
+
+// Vocabulary splits of the forward tile kernel for n_tt token tiles: about
+// one workgroup per CU.
+int forward_splits(int64_t n_tt, int64_t n_vt);
+// Fills the fb_* fields of a plan made by make_plan; block_rows 0 = library choice.
+int plan_forward_backward(Plan* plan, int64_t block_rows);
 
 constexpr size_t kStatusBytes = 256;   // status word at workspace offset 0
 // Backward: the dlogits scale factor and its inverse (two fp32 words) follow
 // the status word.  Powers of two: 1 except for fp16 dlogits (bwd_prep_kernel).
 constexpr size_t kDscaleOffset = 16;
+// One-pass forward + backward: two fp32 ones (a unit factor for kernels that
+// take a dlogits factor pointer).
+constexpr size_t kOnesOffset = 32;
 
 // Partial sums of one finalize block (forward).
 struct BlockPart {
@@ -126,6 +144,21 @@ int launch_chunked(const ChunkPlan& pl, const void* inputs, const void* weight, 
                    float* loss, void* grad_inputs, void* grad_weight, char* ws, hipStream_t st);
 int launch_wmse(const flce_wmse_args& a, int64_t row0, int rows, int V, void* L, int ld, int dtype, float* loss,
                 hipStream_t st);
+
+void launch_forward_rows(const Plan& pl, const void* hidden, const void* weight, const void* bias,
+                         const void* targets, int64_t r0, int rows, int S, float* part, float* loss, float* lse,
+                         BlockPart* blk, void* z, int ldz, hipStream_t st);
+void launch_forward_scalars(const Plan& pl, const BlockPart* blk, int nblk, float* loss, int64_t* num_correct,
+                            float* entropy_sum, int* status, hipStream_t st);
+void launch_prep_rows(const Plan& pl, const void* targets, const float* lse, const float* grad_loss, float* coefA,
+                      float* coefB, float* lseL, int* tgt, int* status, float* dscale, int64_t row0, int64_t row1,
+                      hipStream_t st);
+void launch_gb_reduce(int dtype, const float* part, int n_tt, int ld, int V, void* gb, int accumulate,
+                      const float* dscale, hipStream_t st);
+hipError_t launch_forward_backward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
+                                   const void* targets, const float* grad_loss, float* loss, float* lse,
+                                   int64_t* num_correct, float* entropy_sum, void* grad_hidden, void* grad_weight,
+                                   void* grad_bias, char* ws, hipStream_t st);
 
 hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
                           const void* targets, float* loss, float* lse, int64_t* num_correct,

@@ -152,3 +152,40 @@ def test_chunked_params_layout_and_validation(lib):
     # the built-in loss function checks its arguments on the host
     assert lib.flce_weighted_mse_chunk(None, 0, 1, 10, 16, 16, 1, 16, None) == flce.FLCE_ERR_INVALID_ARG
     assert flce.flce_status_string(flce.FLCE_ERR_CALLBACK) == "the chunk loss function reported an error"
+
+
+def test_forward_backward_workspace_and_validation(lib):
+    def ws(p, rows=0):
+        out = ctypes.c_size_t(0)
+        return lib.flce_forward_backward_workspace_size(ctypes.byref(p), rows, ctypes.byref(out)), out.value
+
+    p = flce.make_params(8192, 4096, 128256, dtype="bf16", reduction="sum", softcap=30.0)
+    rc, b = ws(p)
+    # one 4096-row block of bf16 logits (1.05 GB), the fp32 grad_weight accumulator over the two
+    # blocks (2.1 GB), hidden^T of a block, grad_bias partials: far below N*V + V*H*4 = 4.2 GB
+    assert rc == 0 and 3.1e9 < b < 3.4e9
+    rc, b1 = ws(p, 8192)                     # one block: no fp32 accumulator
+    assert rc == 0 and b1 < b
+    assert ws(p, 100)[0] == flce.FLCE_ERR_UNSUPPORTED
+    assert ws(p, -256)[0] == flce.FLCE_ERR_UNSUPPORTED
+    pf = flce.make_params(8192, 4096, 128256, dtype="bf16", grad_weight_dtype="f32")
+    rc, bf = ws(pf)
+    assert rc == 0 and bf < b - 2e9          # fp32 grad_weight is its own accumulator
+    assert ws(flce.make_params(0, 64, 10))[0] == 0
+    q = flce.make_params(64, 64, 100)
+    big = 1 << 30
+    args = dict(hidden=16, weight=16, bias=None, targets=16, grad_loss=16, loss=16, lse=16, nc=None, ent=None,
+                gh=16, gw=16, gb=None, ws=16, wsb=big)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.flce_forward_backward(ctypes.byref(q), 0, a["hidden"], a["weight"], a["bias"], a["targets"],
+                                         a["grad_loss"], a["loss"], a["lse"], a["nc"], a["ent"], a["gh"], a["gw"],
+                                         a["gb"], a["ws"], a["wsb"], None)
+    assert call(weight=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(gw=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(grad_loss=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(loss=None) == flce.FLCE_ERR_INVALID_ARG
+    assert call(gb=16) == flce.FLCE_ERR_INVALID_ARG          # grad_bias without bias
+    assert call(hidden=18) == flce.FLCE_ERR_UNSUPPORTED
+    assert call(wsb=8) == flce.FLCE_ERR_WORKSPACE_TOO_SMALL

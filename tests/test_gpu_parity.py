@@ -290,14 +290,14 @@ def test_host_validation_errors(flce_lib):
 
 # ----------------------------------------------------------------------------- large workloads
 
-def _sampled_check(flce, wl: si.Workload, n_rows=512, n_vocab=512):
+def _sampled_check(flce, wl: si.Workload, n_rows=512, n_vocab=512, run=None):
     import torch
     c = _from_workload(wl)
     _say(f"[parity-large] {wl.name}: drawing inputs")
     inp = si.make_workload_inputs(wl)
     d = to_device(inp, c.dtype)
     _say(f"[parity-large] {wl.name}: GPU forward+backward")
-    loss, lse, met, gh, gw, gb = _run_gpu(flce, c, d)
+    loss, lse, met, gh, gw, gb = (run or _run_gpu)(flce, c, d)
     loss_n, lse_n = t2np(loss), t2np(lse)
     nc, ent = met["num_correct_tokens"].item(), met["entropy_sum"].item()
     rng = np.random.default_rng(1234)
