@@ -2,17 +2,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-One step is flce_forward followed by flce_backward (loss, LSE, metrics, then
-grad_hidden, grad_weight, grad_bias) on the headline workload: N=8192 tokens,
-H=4096, V=128256, bf16, bias, logit_scale 0.5, softcap 30, 5% ignored
-targets, reduction "sum".  Inputs are seeded synthetic data already resident
-in device memory; outputs and workspaces are allocated before timing.
+One step is a full forward + backward (loss, LSE, metrics, grad_hidden,
+grad_weight, grad_bias) on the headline workload: N=8192 tokens, H=4096,
+V=128256, bf16, bias, logit_scale 0.5, softcap 30, 5% ignored targets,
+reduction "sum".  Two implementations are timed: flce_forward_backward (one
+pass over row blocks, gradients from each block's stored logits: the headline
+`value`) and flce_forward followed by flce_backward (the backward recomputes
+the logit tiles: `split_path`).  Inputs are seeded synthetic data already
+resident in device memory; outputs and workspaces are allocated before timing.
 
-Prints one JSON line.  `value` is tokens/s for the whole step; the step's
-TFLOP/s counts 8*N*H*V (forward logits, recomputed logits and the two
-gradient contractions).  `roofline` reports the forward tile kernel, timed
-with HIP events on the stream it is launched on; `cpu_baseline` times the
-fp64 CPU oracle on a bounded slice of the same workload.
+Prints one JSON line.  `value` is tokens/s for the whole step; `tflops` counts
+the metric's 8*N*H*V (forward logits, recomputed logits and the two gradient
+contractions) per step, `tflops_executed` the 6*N*H*V the one-pass step
+actually runs.  `roofline` reports the forward tile kernel, timed with HIP
+events on the stream it is launched on; `cpu_baseline` times the fp64 CPU
+oracle on a bounded slice of the same workload.
 """
 from __future__ import annotations
 
@@ -117,9 +121,11 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS) + sorted(si.WMSE_WORKLOADS))
-    ap.add_argument("--path", choices=("split", "fused"), default="split",
-                    help="split: flce_forward then flce_backward (the backward recomputes the logit tiles); "
-                         "fused: flce_forward_backward (one pass, gradients from each row block's stored logits)")
+    ap.add_argument("--path", choices=("both", "split", "fused"), default="both",
+                    help="fused: flce_forward_backward (one pass: gradients from each row block's stored "
+                         "logits); split: flce_forward then flce_backward (the backward recomputes the logit "
+                         "tiles); both (default): the fused step is the headline, the split step is reported "
+                         "beside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -136,8 +142,6 @@ def main():
     flce.load()
     if args.workload in si.WMSE_WORKLOADS:
         return run_wmse(args, torch, flce)
-    if args.path == "fused":
-        return run_fused(args, torch, flce)
     wl = si.WORKLOADS[args.workload]
     inp = si.make_workload_inputs(wl)
     d = _to_dev(inp, wl.dtype)
@@ -145,8 +149,6 @@ def main():
     opts = dict(logit_scale=wl.logit_scale, softcap=wl.softcap, z_loss=wl.z_loss,
                 ignore_index=si.IGNORE_INDEX, reduction=wl.reduction)
     pf = flce.make_params(n, h, v, dtype=wl.dtype, grad_weight_dtype=wl.grad_weight_dtype, **opts)
-    ws_f = torch.empty(flce.flce_workspace_size(pf, flce.FLCE_PASS_FORWARD), dtype=torch.uint8, device="cuda")
-    ws_b = torch.empty(flce.flce_workspace_size(pf, flce.FLCE_PASS_BACKWARD), dtype=torch.uint8, device="cuda")
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
     loss = torch.empty(n if wl.reduction == "none" else 1, dtype=torch.float32, device="cuda")
     lse = torch.empty(n, dtype=torch.float32, device="cuda")
@@ -159,18 +161,8 @@ def main():
     P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-
-    def fwd():
-        rc = flce.flce_forward(pf, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]), P(loss),
-                               P(lse), P(nc), P(ent), P(ws_f), ws_f.numel(), sh)
-        if rc:
-            raise flce.FlceError(rc, "flce_forward")
-
-    def bwd():
-        rc = flce.flce_backward(pf, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]), P(lse),
-                                P(gl), P(gh), P(gw), P(gb), P(ws_b), ws_b.numel(), sh)
-        if rc:
-            raise flce.FlceError(rc, "flce_backward")
+    flop8 = 8.0 * n * h * v
+    peak = PEAK_BF16_TFLOPS if wl.dtype in ("bf16", "f16") else PEAK_F32_TFLOPS
 
     if args.copy_calibration_mib:
         nbytes = args.copy_calibration_mib << 20
@@ -179,141 +171,130 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1, e2 in ev:
-        e0.record(stream)
-        fwd()
-        e1.record(stream)
-        bwd()
-        e2.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
-    step_ms = wall / args.steps * 1e3
-    flop = 8.0 * n * h * v
-    tflops = flop / (step_ms * 1e-3) / 1e12
-    fwd_tflops = 2.0 * n * h * v / (fwd_ms * 1e-3) / 1e12
-    bwd_tflops = 6.0 * n * h * v / (bwd_ms * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if wl.dtype in ("bf16", "f16") else PEAK_F32_TFLOPS
+
+    def time_fused():
+        ws = torch.empty(flce.flce_forward_backward_workspace_size(pf, 0), dtype=torch.uint8, device="cuda")
+
+        def step():
+            rc = flce.flce_forward_backward(pf, 0, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]),
+                                            P(gl), P(loss), P(lse), P(nc), P(ent), P(gh), P(gw), P(gb), P(ws),
+                                            ws.numel(), sh)
+            if rc:
+                raise flce.FlceError(rc, "flce_forward_backward")
+
+        torch.cuda.reset_peak_memory_stats()
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        step_ms = (time.perf_counter() - t0) / args.steps * 1e3
+        mem = torch.cuda.max_memory_allocated() / 2**30
+        del ws
+        torch.cuda.empty_cache()
+        return {"ms_per_step": step_ms, "value": n / (step_ms * 1e-3), "peak_mem_gib": mem,
+                "tflops_8nhv": flop8 / (step_ms * 1e-3) / 1e12,
+                "tflops_executed": 0.75 * flop8 / (step_ms * 1e-3) / 1e12}
+
+    def time_split():
+        ws_f = torch.empty(flce.flce_workspace_size(pf, flce.FLCE_PASS_FORWARD), dtype=torch.uint8, device="cuda")
+        ws_b = torch.empty(flce.flce_workspace_size(pf, flce.FLCE_PASS_BACKWARD), dtype=torch.uint8, device="cuda")
+
+        def fwd():
+            rc = flce.flce_forward(pf, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]), P(loss),
+                                   P(lse), P(nc), P(ent), P(ws_f), ws_f.numel(), sh)
+            if rc:
+                raise flce.FlceError(rc, "flce_forward")
+
+        def bwd():
+            rc = flce.flce_backward(pf, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]), P(lse),
+                                    P(gl), P(gh), P(gw), P(gb), P(ws_b), ws_b.numel(), sh)
+            if rc:
+                raise flce.FlceError(rc, "flce_backward")
+
+        torch.cuda.reset_peak_memory_stats()
+        for _ in range(args.warmup):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        # HIP events on the stream the kernels run on bracket each call
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for e0, e1, e2 in ev:
+            e0.record(stream)
+            fwd()
+            e1.record(stream)
+            bwd()
+            e2.record(stream)
+        torch.cuda.synchronize()
+        step_ms = (time.perf_counter() - t0) / args.steps * 1e3
+        fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+        bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+        mem = torch.cuda.max_memory_allocated() / 2**30
+        del ws_f, ws_b
+        torch.cuda.empty_cache()
+        return {"ms_per_step": step_ms, "value": n / (step_ms * 1e-3), "peak_mem_gib": mem,
+                "tflops_8nhv": flop8 / (step_ms * 1e-3) / 1e12, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+                "fwd_tflops": 0.25 * flop8 / (fwd_ms * 1e-3) / 1e12,
+                "bwd_tflops": 0.75 * flop8 / (bwd_ms * 1e-3) / 1e12}
+
+    fused = time_fused() if args.path in ("both", "fused") else None
+    split = time_split() if args.path in ("both", "split") else None
+    head = fused if fused is not None else split
+    cfg = {"workload": wl.name, "n_tokens": n, "hidden": h, "vocab": v, "bias": wl.bias_std is not None,
+           "logit_scale": wl.logit_scale, "softcap": wl.softcap, "z_loss": wl.z_loss,
+           "ignore_frac": wl.ignore_frac, "reduction": wl.reduction,
+           "grad_weight_dtype": wl.grad_weight_dtype or wl.dtype,
+           "path": ("flce_forward_backward (one pass, no recompute)" if fused is not None
+                    else "flce_forward + flce_backward (recompute)")}
     out = {
         "metric": METRIC,
-        "value": n / (step_ms * 1e-3),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": step_ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "n_tokens": n, "hidden": h, "vocab": v,
-                   "bias": wl.bias_std is not None, "logit_scale": wl.logit_scale, "softcap": wl.softcap,
-                   "z_loss": wl.z_loss, "ignore_frac": wl.ignore_frac, "reduction": wl.reduction,
-                   "grad_weight_dtype": wl.grad_weight_dtype or wl.dtype},
-        "tflops": tflops,
-        "frac_of_peak": tflops / peak,
-        "fwd_ms": fwd_ms,
-        "bwd_ms": bwd_ms,
-        "fwd_tflops": fwd_tflops,
-        "bwd_tflops": bwd_tflops,
-        "peak_mem_gib": torch.cuda.max_memory_allocated() / 2**30,
+        "config": cfg,
+        # the metric's count: 8NHV flop per step (forward logits, recomputed logits, two contractions)
+        "tflops": head["tflops_8nhv"],
+        "frac_of_peak": head["tflops_8nhv"] / peak,
+        "peak_mem_gib": head["peak_mem_gib"],
         "device": _device_info(torch),
-        # the forward call is the vocabulary-tiled logit kernel plus two small
-        # finalize kernels; its HIP-event time bounds the tile kernel's time
-        "roofline": {"bound": "mfma", "kernel": "fwd_tiles_kernel (+ finalize)",
-                     "achieved": fwd_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": fwd_tflops / peak, "traffic": measured_traffic(wl.name)},
         "kernel_source_hash": kernel_source_hash(),
     }
+    if fused is not None:
+        # the one-pass step executes 6NHV (no recompute)
+        out["tflops_executed"] = fused["tflops_executed"]
+        out["frac_of_peak_executed"] = fused["tflops_executed"] / peak
+    if split is not None:
+        if fused is not None:
+            out["split_path"] = {"path": "flce_forward + flce_backward (backward recomputes the logit tiles)",
+                                 "ms_per_step": split["ms_per_step"], "value": split["value"],
+                                 "unit": "tokens/s", "tflops": split["tflops_8nhv"],
+                                 "frac_of_peak": split["tflops_8nhv"] / peak, "fwd_ms": split["fwd_ms"],
+                                 "bwd_ms": split["bwd_ms"], "fwd_tflops": split["fwd_tflops"],
+                                 "bwd_tflops": split["bwd_tflops"], "peak_mem_gib": split["peak_mem_gib"]}
+        else:
+            out.update({k: split[k] for k in ("fwd_ms", "bwd_ms", "fwd_tflops", "bwd_tflops")})
+        # the forward tile kernel (flce_forward = the tile kernel plus two finalize kernels of
+        # ~5 us), timed with HIP events on its stream; the one-pass step runs the same kernel
+        # with the logit store on top
+        out["roofline"] = {"bound": "mfma", "kernel": "fwd_tiles_kernel (flce_forward: + finalize)",
+                           "achieved": split["fwd_tflops"], "peak": peak, "unit": "TFLOP/s",
+                           "frac": split["fwd_tflops"] / peak, "traffic": measured_traffic(wl.name)}
     if not args.no_cpu_baseline:
         del d
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(inp, wl, min(args.cpu_rows, n))
-    print(json.dumps(out), flush=True)
-
-
-def run_fused(args, torch, flce):
-    """One step = one flce_forward_backward call: per block of rows, the logit
-    tiles (2 x rows x H x V, stored in the input dtype), the logit gradient in
-    place, grad_hidden and grad_weight (2 x rows x H x V each): 6NHV flop
-    executed.  TFLOP/s is also given on the metric's 8NHV count."""
-    wl = si.WORKLOADS[args.workload]
-    inp = si.make_workload_inputs(wl)
-    d = _to_dev(inp, wl.dtype)
-    n, h, v = wl.n_tokens, wl.hidden, wl.vocab
-    opts = dict(logit_scale=wl.logit_scale, softcap=wl.softcap, z_loss=wl.z_loss,
-                ignore_index=si.IGNORE_INDEX, reduction=wl.reduction)
-    pf = flce.make_params(n, h, v, dtype=wl.dtype, grad_weight_dtype=wl.grad_weight_dtype, **opts)
-    ws = torch.empty(flce.flce_forward_backward_workspace_size(pf, 0), dtype=torch.uint8, device="cuda")
-    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
-    loss = torch.empty(n if wl.reduction == "none" else 1, dtype=torch.float32, device="cuda")
-    lse = torch.empty(n, dtype=torch.float32, device="cuda")
-    nc = torch.empty(1, dtype=torch.int64, device="cuda")
-    ent = torch.empty(1, dtype=torch.float32, device="cuda")
-    gh = torch.empty((n, h), dtype=tdt[wl.dtype], device="cuda")
-    gw = torch.empty((v, h), dtype=tdt[wl.grad_weight_dtype or wl.dtype], device="cuda")
-    gb = torch.empty(v, dtype=tdt[wl.dtype], device="cuda") if d["bias"] is not None else None
-    gl = d["grad_loss"] if wl.reduction == "none" else d["grad_loss"][:1]
-    P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-    stream = torch.cuda.current_stream()
-
-    def step():
-        rc = flce.flce_forward_backward(pf, 0, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]), P(gl),
-                                        P(loss), P(lse), P(nc), P(ent), P(gh), P(gw), P(gb), P(ws), ws.numel(),
-                                        stream.cuda_stream)
-        if rc:
-            raise flce.FlceError(rc, "flce_forward_backward")
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = wall / args.steps * 1e3
-    ev_ms = float(np.mean([x.elapsed_time(z) for x, z in ev]))
-    peak = PEAK_BF16_TFLOPS if wl.dtype in ("bf16", "f16") else PEAK_F32_TFLOPS
-    out = {
-        "metric": METRIC,
-        "value": n / (step_ms * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": step_ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": wl.dtype,
-        "data": "synthetic",
-        "config": {"workload": wl.name, "path": "fused (flce_forward_backward)", "n_tokens": n, "hidden": h,
-                   "vocab": v, "bias": wl.bias_std is not None, "logit_scale": wl.logit_scale,
-                   "softcap": wl.softcap, "z_loss": wl.z_loss, "ignore_frac": wl.ignore_frac,
-                   "reduction": wl.reduction, "grad_weight_dtype": wl.grad_weight_dtype or wl.dtype},
-        "tflops_8nhv": 8.0 * n * h * v / (step_ms * 1e-3) / 1e12,
-        "frac_of_peak_8nhv": 8.0 * n * h * v / (step_ms * 1e-3) / 1e12 / peak,
-        "tflops_executed_6nhv": 6.0 * n * h * v / (step_ms * 1e-3) / 1e12,
-        "frac_of_peak_executed": 6.0 * n * h * v / (step_ms * 1e-3) / 1e12 / peak,
-        "event_ms_per_step": ev_ms,
-        "peak_mem_gib": torch.cuda.max_memory_allocated() / 2**30,
-        "device": _device_info(torch),
-        "kernel_source_hash": kernel_source_hash(),
-    }
     print(json.dumps(out), flush=True)
 
 

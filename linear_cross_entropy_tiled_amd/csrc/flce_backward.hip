@@ -363,6 +363,96 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// grad_weight epilogue for a wave whose 128 (h) x 64 (v) block lies inside the
+// matrix: straight-line code per (mode, output type, accumulate), and per half
+// MFMA tile every read (the fp32 accumulator, the prior output) is issued
+// before the first store, so the reads overlap instead of each waiting for the
+// stores before it.  Lane: 4 consecutive h of one v per 4-register group.
+// ---------------------------------------------------------------------------
+template <typename OutT> __device__ __forceinline__ f32x4 load4v(const OutT* p);
+template <> __device__ __forceinline__ f32x4 load4v<float>(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+template <> __device__ __forceinline__ f32x4 load4v<bf16>(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+template <> __device__ __forceinline__ f32x4 load4v<f16>(const f16* p) {
+  const f16x4 v = *reinterpret_cast<const f16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+template <typename T> constexpr bool is_f16() { return false; }
+template <> constexpr bool is_f16<f16>() { return true; }
+
+// MODE 0: acc32 = C; 1: acc32 += C; 2: out = acc32 + C; 3: out = C; ACC (modes
+// 2, 3): plus out's prior contents.  C = the accumulator times `inv`; row r of
+// the wave's block is row rbase + r of the ld-wide matrices, column c is
+// column cbase + c.
+template <typename OutT, int MODE, bool ACC>
+__device__ __forceinline__ void block_store_t(float* acc32, OutT* out, int ld,
+                                              const f32x16 (&acc)[kMI][kNI], float inv, int rbase, int cbase,
+                                              int lane) {
+  constexpr bool READ_ACC = MODE == 1 || MODE == 2;
+  constexpr bool READ_OUT = ACC && MODE >= 2;
+#pragma unroll
+  for (int ni = 0; ni < kNI; ni++) {
+    const size_t row = (size_t)(rbase + ni * 32 + (lane & 31)) * ld + cbase + 4 * (lane >> 5);
+#pragma unroll
+    for (int m0 = 0; m0 < kMI; m0 += 2) {
+      f32x4 pa[2][4], po[2][4];
+#pragma unroll
+      for (int mi = 0; mi < 2; mi++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          const size_t o = row + (m0 + mi) * 32 + 8 * g;
+          if constexpr (READ_ACC) pa[mi][g] = *reinterpret_cast<const f32x4*>(acc32 + o);
+          if constexpr (READ_OUT) po[mi][g] = load4v<OutT>(out + o);
+        }
+#pragma unroll
+      for (int mi = 0; mi < 2; mi++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          const size_t o = row + (m0 + mi) * 32 + 8 * g;
+          float c[4];
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            c[j] = acc[m0 + mi][ni][4 * g + j] * inv;
+            if constexpr (READ_ACC) c[j] += pa[mi][g][j];
+            if constexpr (READ_OUT) c[j] += po[mi][g][j];
+          }
+          if constexpr (MODE <= 1) store4(acc32 + o, c[0], c[1], c[2], c[3]);
+          else store4(out + o, c[0], c[1], c[2], c[3]);
+        }
+    }
+  }
+}
+
+// Modes 2 and 3 into an output of type OutT.
+template <typename OutT>
+__device__ __forceinline__ void block_store_out(float* acc32, void* out, int ld, int mode, bool accumulate,
+                                                const f32x16 (&acc)[kMI][kNI], float inv, int rbase, int cbase,
+                                                int lane) {
+  OutT* o = reinterpret_cast<OutT*>(out);
+  if (mode == 2) {
+    if (accumulate) block_store_t<OutT, 2, true>(acc32, o, ld, acc, inv, rbase, cbase, lane);
+    else block_store_t<OutT, 2, false>(acc32, o, ld, acc, inv, rbase, cbase, lane);
+  } else {
+    if (accumulate) block_store_t<OutT, 3, true>(acc32, o, ld, acc, inv, rbase, cbase, lane);
+    else block_store_t<OutT, 3, false>(acc32, o, ld, acc, inv, rbase, cbase, lane);
+  }
+}
+
+// Any mode; out_type is the flce_dtype of `out` (modes 2, 3).
+__device__ __forceinline__ void block_store(float* acc32, void* out, int out_type, int ld, int mode, bool accumulate,
+                                            const f32x16 (&acc)[kMI][kNI], float inv, int rbase, int cbase,
+                                            int lane) {
+  if (mode == 0) block_store_t<float, 0, false>(acc32, nullptr, ld, acc, inv, rbase, cbase, lane);
+  else if (mode == 1) block_store_t<float, 1, false>(acc32, nullptr, ld, acc, inv, rbase, cbase, lane);
+  else if (out_type == FLCE_BF16) block_store_out<bf16>(acc32, out, ld, mode, accumulate, acc, inv, rbase, cbase, lane);
+  else if (out_type == FLCE_F16) block_store_out<f16>(acc32, out, ld, mode, accumulate, acc, inv, rbase, cbase, lane);
+  else block_store_out<float>(acc32, out, ld, mode, accumulate, acc, inv, rbase, cbase, lane);
+}
+
+// ---------------------------------------------------------------------------
 // grad_weight for one chunk: C[h][v] = sum_t hidden[t][h] D[t][v]
 // A = hidden (MNMAJOR: rows t, cols h), B = D (MNMAJOR: rows t, cols v).
 // ---------------------------------------------------------------------------
@@ -397,6 +487,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gw_kernel(GwArgs a) {
   tile_mainloop<T, true, false>(da, db, KT, grouped_share(ht, vt), acc);
 
   const float inv = a.dscale[1];
+  const int vbase = a.cv0 + vl0 + wn * kWaveN, hbase = h0 + wm * kWaveM;
+  if (vbase + kWaveN <= a.V && hbase + kWaveM <= a.H) {   // the wave's block lies inside grad_weight
+    block_store(a.acc32, a.gw, a.gw_type, a.H, a.mode, a.accumulate != 0, acc, inv, vbase, hbase, lane);
+    return;
+  }
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
     const int v = a.cv0 + vl0 + wn * kWaveN + ni * 32 + (lane & 31);
@@ -470,6 +565,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gh_kernel(GhArgs a) {
   tile_mainloop<T, false, true>(da, db, KT, grouped_share(ht, tt), acc);
 
   const float inv = a.dscale[1];
+  const int tbase = t0 + wn * kWaveN, hbase = h0 + wm * kWaveM;
+  if (tbase + kWaveN <= a.N && hbase + kWaveM <= a.H) {   // the wave's block lies inside grad_hidden
+    if (a.parts > 1)   // partial of this split; bwd_gh_reduce applies the mode
+      block_store(a.part + (size_t)split * a.N * a.H, nullptr, FLCE_F32, a.H, 0, false, acc, inv, tbase, hbase, lane);
+    else
+      block_store(a.accb, a.out, a.out_f32 ? FLCE_F32 : (sizeof(T) == 2 ? (is_f16<T>() ? FLCE_F16 : FLCE_BF16) : FLCE_F32),
+                  a.H, a.mode, false, acc, inv, tbase, hbase, lane);
+    return;
+  }
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
     const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);

@@ -49,11 +49,13 @@ def test_forward_backward_parity(flce_lib, case, block_rows):
     _check_against_oracle(c, inp, _run_fused(flce_lib, c, d, block_rows))
 
 
-def test_forward_backward_accumulates(flce_lib):
+@pytest.mark.parametrize("h", [72, 256])
+def test_forward_backward_accumulates(flce_lib, h):
     """FLCE_ACCUMULATE_GRAD_WEIGHT / _BIAS over several blocks (bf16 grad_weight: the fp32
-    accumulator's last block adds the prior contents)."""
+    accumulator's last block adds the prior contents); H = 256 takes the epilogue form for
+    blocks inside the matrix."""
     import torch
-    c = Case("fused_accumulate", 700, 72, 3000, "bf16", 0.1, 0.8, 3.0, 1e-3, 0.1, "mean", weight_std=0.1, seed=23)
+    c = Case("fused_accumulate", 700, h, 3000, "bf16", 0.1, 0.8, 3.0, 1e-3, 0.1, "mean", weight_std=0.1, seed=23)
     inp = _inputs(c)
     d = to_device(inp, c.dtype)
     X, W, B, T = widened(inp, c.dtype)

@@ -137,12 +137,15 @@ def _ws_probe(flce, d):
     return ws
 
 
+@pytest.mark.parametrize("h", [72, 256])
 @pytest.mark.parametrize("gw_dtype", ["bf16", "f32"])
-def test_accumulate_into_grad_weight_and_bias(flce_lib, gw_dtype):
+def test_accumulate_into_grad_weight_and_bias(flce_lib, gw_dtype, h):
     """FLCE_ACCUMULATE_GRAD_WEIGHT / _BIAS: the backward adds to the buffers' contents
-    (two vocabulary chunks, so every chunk's grad_weight rows take the add)."""
+    (two vocabulary chunks, so every chunk's grad_weight rows take the add).  H = 72 leaves
+    every wave's block partly outside the matrix, H = 256 puts most inside (the two
+    epilogue forms)."""
     import torch
-    c = Case("accumulate", 300, 72, 33000, "bf16", 0.1, 0.8, 3.0, 1e-3, 0.1, "mean", gw_dtype,
+    c = Case("accumulate", 300, h, 33000, "bf16", 0.1, 0.8, 3.0, 1e-3, 0.1, "mean", gw_dtype,
              weight_std=0.1, seed=21)
     inp = _inputs(c)
     d = to_device(inp, c.dtype)
