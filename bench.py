@@ -126,6 +126,8 @@ def main():
                          "logits); split: flce_forward then flce_backward (the backward recomputes the logit "
                          "tiles); both (default): the fused step is the headline, the split step is reported "
                          "beside it")
+    ap.add_argument("--block-rows", type=int, default=0,
+                    help="rows per block of flce_forward_backward (a multiple of 256; 0 = the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -173,10 +175,11 @@ def main():
         del src, dst
 
     def time_fused():
-        ws = torch.empty(flce.flce_forward_backward_workspace_size(pf, 0), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(flce.flce_forward_backward_workspace_size(pf, args.block_rows), dtype=torch.uint8,
+                         device="cuda")
 
         def step():
-            rc = flce.flce_forward_backward(pf, 0, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]),
+            rc = flce.flce_forward_backward(pf, args.block_rows, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]),
                                             P(gl), P(loss), P(lse), P(nc), P(ent), P(gh), P(gw), P(gb), P(ws),
                                             ws.numel(), sh)
             if rc:
@@ -247,7 +250,7 @@ def main():
     cfg = {"workload": wl.name, "n_tokens": n, "hidden": h, "vocab": v, "bias": wl.bias_std is not None,
            "logit_scale": wl.logit_scale, "softcap": wl.softcap, "z_loss": wl.z_loss,
            "ignore_frac": wl.ignore_frac, "reduction": wl.reduction,
-           "grad_weight_dtype": wl.grad_weight_dtype or wl.dtype,
+           "grad_weight_dtype": wl.grad_weight_dtype or wl.dtype, "block_rows": args.block_rows or "library choice",
            "path": ("flce_forward_backward (one pass, no recompute)" if fused is not None
                     else "flce_forward + flce_backward (recompute)")}
     out = {

@@ -142,3 +142,31 @@ def test_forward_backward_f16_small_gradients(flce_lib):
 @pytest.mark.parametrize("name", ["bf16_n8192_h4096_v128256", "bf16_n16384_h2048_v256000"])
 def test_forward_backward_full_size_sampled(flce_lib, name):
     _sampled_check(flce_lib, si.WORKLOADS[name], run=lambda f, c, d: _run_fused(f, c, d, 0))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_forward_backward_int32_targets(flce_lib, dtype):
+    """int32 targets give the same bits as the same targets in int64 (several blocks)."""
+    import torch
+    c = Case("fused_int32_targets", 700, 200, 1500, dtype, 0.1, 0.7, 2.0, 0.01, 0.1, "mean", weight_std=0.1)
+    d = to_device(_inputs(c), c.dtype)
+    r64 = _run_fused(flce_lib, c, d, 256)
+    d32 = dict(d)
+    d32["targets"] = d["targets"].to(torch.int32)
+    r32 = _run_fused(flce_lib, c, d32, 256)
+    for name, a, b in zip(("loss", "lse", "grad_hidden", "grad_weight", "grad_bias"),
+                          (r64[0], r64[1], r64[3], r64[4], r64[5]), (r32[0], r32[1], r32[3], r32[4], r32[5])):
+        assert torch.equal(a, b), name
+    assert r64[2]["num_correct_tokens"].item() == r32[2]["num_correct_tokens"].item()
+
+
+def test_forward_backward_deterministic(flce_lib):
+    """Same inputs, same bits, run to run (no float atomics anywhere)."""
+    import torch
+    c = Case("fused_determinism", 600, 192, 3000, "bf16", 0.1, 0.8, 8.0, 1e-3, 0.1, "sum", weight_std=0.1)
+    d = to_device(_inputs(c), c.dtype)
+    a = _run_fused(flce_lib, c, d, 256)
+    b = _run_fused(flce_lib, c, d, 256)
+    for i, name in ((0, "loss"), (1, "lse"), (3, "grad_hidden"), (4, "grad_weight"), (5, "grad_bias")):
+        assert torch.equal(a[i], b[i]), name
+    assert torch.equal(a[2]["entropy_sum"], b[2]["entropy_sum"])
