@@ -128,6 +128,9 @@ def main():
                          "beside it")
     ap.add_argument("--block-rows", type=int, default=0,
                     help="rows per block of flce_forward_backward (a multiple of 256; 0 = the library's choice)")
+    ap.add_argument("--grad-weight-accum", choices=("fp32", "weight"), default="fp32",
+                    help="flce_forward_backward: sum grad_weight over the row blocks in fp32 (default) or in its "
+                         "own dtype")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -150,7 +153,8 @@ def main():
     n, h, v = wl.n_tokens, wl.hidden, wl.vocab
     opts = dict(logit_scale=wl.logit_scale, softcap=wl.softcap, z_loss=wl.z_loss,
                 ignore_index=si.IGNORE_INDEX, reduction=wl.reduction)
-    pf = flce.make_params(n, h, v, dtype=wl.dtype, grad_weight_dtype=wl.grad_weight_dtype, **opts)
+    pf = flce.make_params(n, h, v, dtype=wl.dtype, grad_weight_dtype=wl.grad_weight_dtype,
+                          grad_weight_accum_dtype=args.grad_weight_accum, **opts)
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
     loss = torch.empty(n if wl.reduction == "none" else 1, dtype=torch.float32, device="cuda")
     lse = torch.empty(n, dtype=torch.float32, device="cuda")
@@ -251,6 +255,7 @@ def main():
            "logit_scale": wl.logit_scale, "softcap": wl.softcap, "z_loss": wl.z_loss,
            "ignore_frac": wl.ignore_frac, "reduction": wl.reduction,
            "grad_weight_dtype": wl.grad_weight_dtype or wl.dtype, "block_rows": args.block_rows or "library choice",
+           "grad_weight_accum_dtype": args.grad_weight_accum,
            "path": ("flce_forward_backward (one pass, no recompute)" if fused is not None
                     else "flce_forward + flce_backward (recompute)")}
     out = {

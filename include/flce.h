@@ -77,11 +77,20 @@ typedef enum { FLCE_PASS_FORWARD = 0, FLCE_PASS_BACKWARD = 1 } flce_pass;
  * Linear Loss" page, "Weight-gradient accumulation dtype": accumulate in the
  * weight dtype, or in fp32 with grad_weight_dtype = FLCE_F32).  The sum is
  * formed in fp32 and rounded once to the buffer's dtype.
- * FLCE_TARGETS_INT32 (both passes): `targets` points to int32 values. */
+ * FLCE_TARGETS_INT32 (both passes): `targets` points to int32 values.
+ * FLCE_GRAD_WEIGHT_ACCUM_IN_OUTPUT (flce_forward_backward): sum grad_weight
+ * over the row blocks in grad_weight's own dtype, rounding after every block,
+ * instead of in an fp32 workspace accumulator rounded once ("Chunked Linear
+ * Cross-Entropy" page, "Usage": grad_weight_accum_dtype="weight"; "Chunked
+ * Linear Loss" page, "Weight-gradient accumulation dtype": less memory and
+ * faster, rounds between chunks).  No effect when grad_weight is fp32 or the
+ * call has one block, nor on flce_backward, which writes each grad_weight row
+ * once. */
 typedef enum {
   FLCE_ACCUMULATE_GRAD_WEIGHT = 1,
   FLCE_ACCUMULATE_GRAD_BIAS = 2,
-  FLCE_TARGETS_INT32 = 4
+  FLCE_TARGETS_INT32 = 4,
+  FLCE_GRAD_WEIGHT_ACCUM_IN_OUTPUT = 8
 } flce_flags;
 
 typedef struct {

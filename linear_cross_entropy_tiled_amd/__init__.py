@@ -42,6 +42,7 @@ FLCE_PASS_BACKWARD = 1
 FLCE_ACCUMULATE_GRAD_WEIGHT = 1
 FLCE_ACCUMULATE_GRAD_BIAS = 2
 FLCE_TARGETS_INT32 = 4
+FLCE_GRAD_WEIGHT_ACCUM_IN_OUTPUT = 8
 
 EXPORTED = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_get_status",
             "flce_status_string", "flce_version", "flce_chunked_workspace_size",
@@ -232,7 +233,8 @@ def make_params(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
                 grad_weight_dtype: Optional[str] = None, logit_scale: float = 1.0,
                 softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
                 reduction: str = "mean", accumulate_grad_weight: bool = False,
-                accumulate_grad_bias: bool = False, targets_int32: bool = False) -> flce_params:
+                accumulate_grad_bias: bool = False, targets_int32: bool = False,
+                grad_weight_accum_dtype: str = "fp32") -> flce_params:
     if reduction not in REDUCTIONS:
         raise ValueError(f"invalid reduction {reduction!r}")
     dt = DTYPES
@@ -247,6 +249,10 @@ def make_params(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
     p.flags = (FLCE_ACCUMULATE_GRAD_WEIGHT if accumulate_grad_weight else 0) | \
               (FLCE_ACCUMULATE_GRAD_BIAS if accumulate_grad_bias else 0) | \
               (FLCE_TARGETS_INT32 if targets_int32 else 0)
+    if grad_weight_accum_dtype not in ("fp32", "weight"):
+        raise ValueError(f"invalid grad_weight_accum_dtype {grad_weight_accum_dtype!r}")
+    if grad_weight_accum_dtype == "weight":
+        p.flags |= FLCE_GRAD_WEIGHT_ACCUM_IN_OUTPUT
     return p
 
 
@@ -358,11 +364,13 @@ def backward(hidden, weight, targets, lse, grad_loss, bias=None, *, logit_scale:
 def forward_backward(hidden, weight, targets, grad_loss, bias=None, *, logit_scale: float = 1.0,
                      softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
                      reduction: str = "mean", grad_weight_dtype: Optional[str] = None, return_metrics: bool = False,
-                     block_rows: int = 0, workspace=None, grad_weight=None, grad_bias=None):
+                     block_rows: int = 0, grad_weight_accum_dtype: str = "fp32", workspace=None, grad_weight=None,
+                     grad_bias=None):
     """Runs flce_forward_backward (loss and gradients in one pass, the upstream gradient
     ``grad_loss`` given up front) on the current stream.  Returns
     (loss, lse, metrics | None, grad_hidden, grad_weight, grad_bias); ``grad_weight`` /
-    ``grad_bias`` given: accumulated into in place, as in ``backward``."""
+    ``grad_bias`` given: accumulated into in place, as in ``backward``.  ``grad_weight_accum_dtype``:
+    "fp32" (sum over the row blocks in fp32, round once) or "weight" (sum in grad_weight's dtype)."""
     import torch
     for t, n in ((hidden, "hidden"), (weight, "weight"), (targets, "targets"), (bias, "bias"),
                  (grad_loss, "grad_loss"), (grad_weight, "grad_weight"), (grad_bias, "grad_bias")):
@@ -379,7 +387,7 @@ def forward_backward(hidden, weight, targets, grad_loss, bias=None, *, logit_sca
     p = make_params(n, h, v, dtype=dt, grad_weight_dtype=grad_weight_dtype, logit_scale=logit_scale,
                     softcap=softcap, z_loss=z_loss, ignore_index=ignore_index, reduction=reduction,
                     accumulate_grad_weight=grad_weight is not None, accumulate_grad_bias=grad_bias is not None,
-                    targets_int32=_targets_int32(targets))
+                    targets_int32=_targets_int32(targets), grad_weight_accum_dtype=grad_weight_accum_dtype)
     dev = hidden.device
     ws_bytes = flce_forward_backward_workspace_size(p, block_rows)
     if workspace is None or workspace.numel() < ws_bytes:

@@ -48,7 +48,8 @@ int make_plan(const flce_params* p, Plan* pl) {
   if (p->reduction != FLCE_REDUCTION_NONE && p->reduction != FLCE_REDUCTION_SUM &&
       p->reduction != FLCE_REDUCTION_MEAN)
     return FLCE_ERR_INVALID_ARG;
-  if ((p->flags & ~(FLCE_ACCUMULATE_GRAD_WEIGHT | FLCE_ACCUMULATE_GRAD_BIAS | FLCE_TARGETS_INT32)) != 0 ||
+  if ((p->flags & ~(FLCE_ACCUMULATE_GRAD_WEIGHT | FLCE_ACCUMULATE_GRAD_BIAS | FLCE_TARGETS_INT32 |
+                    FLCE_GRAD_WEIGHT_ACCUM_IN_OUTPUT)) != 0 ||
       p->reserved_f != 0.0f)
     return FLCE_ERR_INVALID_ARG;
   if (!isfinite(p->logit_scale) || !isfinite(p->softcap) || !isfinite(p->z_loss) || p->z_loss < 0.0f)
@@ -72,6 +73,7 @@ int make_plan(const flce_params* p, Plan* pl) {
   P.accum_gw = (p->flags & FLCE_ACCUMULATE_GRAD_WEIGHT) != 0;
   P.accum_gb = (p->flags & FLCE_ACCUMULATE_GRAD_BIAS) != 0;
   P.tgt_i32 = (p->flags & FLCE_TARGETS_INT32) != 0;
+  P.gw_accum_out = (p->flags & FLCE_GRAD_WEIGHT_ACCUM_IN_OUTPUT) != 0;
   P.scale = p->logit_scale;
   P.cap = p->softcap > 0.0f ? p->softcap : 0.0f;
   P.z_loss = p->z_loss;
@@ -228,7 +230,7 @@ int plan_forward_backward(Plan* pl, int64_t block_rows) {
   if (vc > P.V_pad) vc = P.V_pad;
   P.fb_Vc = vc;
   P.fb_vchunks = (int)((P.V_pad + vc - 1) / vc);
-  P.fb_gw_acc32 = P.gw_dtype != FLCE_F32 && P.fb_blocks > 1;
+  P.fb_gw_acc32 = P.gw_dtype != FLCE_F32 && P.fb_blocks > 1 && !P.gw_accum_out;
   const int64_t last = P.N > 0 ? P.N - (int64_t)(P.fb_blocks - 1) * rows : 0;
   const int64_t full_tt = rows / 256, last_tt = (last + 255) / 256;
 

@@ -240,7 +240,7 @@ hipError_t launch_forward_backward(const Plan& pl, const void* hidden, const voi
     if (pl.fb_gw_acc32) {   // fp32 sum over the blocks, rounded once at the end
       g.mode = first && last ? 3 : (first ? 0 : (last ? 2 : 1));
       g.accumulate = pl.accum_gw ? 1 : 0;
-    } else {                // fp32 output (or one block): summed in the output buffer
+    } else {                // fp32 output, one block, or summed in the output's dtype on request
       g.mode = 3;
       g.accumulate = (!first || pl.accum_gw) ? 1 : 0;
     }

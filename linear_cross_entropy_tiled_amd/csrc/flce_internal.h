@@ -16,6 +16,7 @@ struct Plan {
   bool has_bias;
   bool accum_gw, accum_gb;       // backward adds into grad_weight / grad_bias
   bool tgt_i32;                  // targets are int32 (else int64)
+  bool gw_accum_out;             // one-pass path: sum grad_weight over the blocks in its own dtype
   float scale, cap, z_loss;
 
   int64_t n_tt, n_vt, n_ht;      // 256-wide tiles over tokens, vocabulary, hidden

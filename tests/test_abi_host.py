@@ -70,7 +70,7 @@ def test_workspace_sizes(lib):
     ("dtype", 7, flce.FLCE_ERR_INVALID_ARG),
     ("grad_weight_dtype", 9, flce.FLCE_ERR_INVALID_ARG),
     ("reduction", 3, flce.FLCE_ERR_INVALID_ARG),
-    ("flags", 8, flce.FLCE_ERR_INVALID_ARG),
+    ("flags", 16, flce.FLCE_ERR_INVALID_ARG),
     ("z_loss", -1.0, flce.FLCE_ERR_INVALID_ARG),
     ("logit_scale", float("inf"), flce.FLCE_ERR_INVALID_ARG),
 ])
@@ -171,6 +171,10 @@ def test_forward_backward_workspace_and_validation(lib):
     pf = flce.make_params(8192, 4096, 128256, dtype="bf16", grad_weight_dtype="f32")
     rc, bf = ws(pf)
     assert rc == 0 and bf < b - 2e9          # fp32 grad_weight is its own accumulator
+    pw = flce.make_params(8192, 4096, 128256, dtype="bf16", reduction="sum", grad_weight_accum_dtype="weight")
+    rc, bw = ws(pw)
+    assert rc == 0 and bw < b - 2e9          # summed in grad_weight's dtype: no fp32 accumulator
+    assert pw.flags == flce.FLCE_GRAD_WEIGHT_ACCUM_IN_OUTPUT
     assert ws(flce.make_params(0, 64, 10))[0] == 0
     q = flce.make_params(64, 64, 100)
     big = 1 << 30

@@ -170,3 +170,19 @@ def test_forward_backward_deterministic(flce_lib):
     for i, name in ((0, "loss"), (1, "lse"), (3, "grad_hidden"), (4, "grad_weight"), (5, "grad_bias")):
         assert torch.equal(a[i], b[i]), name
     assert torch.equal(a[2]["entropy_sum"], b[2]["entropy_sum"])
+
+
+def test_forward_backward_grad_weight_accumulated_in_weight_dtype(flce_lib):
+    """grad_weight_accum_dtype="weight" (FLCE_GRAD_WEIGHT_ACCUM_IN_OUTPUT): the blocks' grad_weight
+    contributions are summed in bf16, rounding after each of the three blocks; still within the
+    gradient tolerance, and not bitwise the fp32-accumulated result."""
+    import torch
+    c = Case("fused_accum_weight_dtype", 700, 256, 3000, "bf16", 0.1, 0.8, 3.0, 1e-3, 0.1, "mean", weight_std=0.1,
+             seed=29)
+    inp = _inputs(c)
+    d = to_device(inp, c.dtype)
+    out_w = _run_fused(flce_lib, c, d, 256, grad_weight_accum_dtype="weight")
+    rgh, rgw, rgb = _check_against_oracle(c, inp, out_w)
+    out_f = _run_fused(flce_lib, c, d, 256)
+    assert torch.equal(out_w[3], out_f[3])            # grad_hidden does not depend on it
+    assert not torch.equal(out_w[4], out_f[4])
