@@ -411,6 +411,35 @@ def forward_backward(hidden, weight, targets, grad_loss, bias=None, *, logit_sca
     return loss, lse, metrics, gh, gw, gb
 
 
+def linear_cross_entropy(hidden, weight, targets, bias=None, *, logit_scale: float = 1.0,
+                         softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
+                         reduction: str = "mean"):
+    """The loss as a differentiable torch op: flce_forward now, flce_backward (which recomputes
+    the logit tiles from hidden, weight and the saved LSE) when autograd asks for gradients,
+    with the upstream gradient autograd supplies.  Returns the loss (a scalar, or (N,) for
+    "none")."""
+    import torch
+
+    opts = dict(logit_scale=logit_scale, softcap=softcap, z_loss=z_loss, ignore_index=ignore_index,
+                reduction=reduction)
+
+    class _Fn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, w, b):
+            loss, lse, _ = forward(x, w, targets, b, **opts)
+            ctx.save_for_backward(x, w, b, lse)
+            return loss
+
+        @staticmethod
+        def backward(ctx, g):
+            x, w, b, lse = ctx.saved_tensors
+            g = g.detach().to(torch.float32).contiguous().reshape(-1)
+            gh, gw, gb = backward(x, w, targets, lse, g, b, **opts)   # gradients in the inputs' dtypes
+            return gh, gw, gb
+
+    return _Fn.apply(hidden, weight, bias)
+
+
 def get_status(workspace) -> int:
     return flce_get_status(_ptr(workspace), _stream_handle(workspace.device))
 

@@ -391,3 +391,26 @@ def test_f16_small_gradients_keep_precision(flce_lib):
     for what, a, r in (("grad_hidden", t2np(gh), rgh), ("grad_weight", t2np(gw), rgw), ("grad_bias", t2np(gb), rgb)):
         err = np.abs(a - r).max() / np.abs(r).max()
         assert err <= 2e-3, f"{what}: {err:.3e}"
+
+
+def test_autograd_function(flce_lib):
+    """linear_cross_entropy under torch autograd: the loss and the leaf gradients equal the
+    direct flce_forward / flce_backward calls with the upstream gradient autograd passes
+    (here 2.5 for "sum", a vector for "none")."""
+    import torch
+    for red in ("sum", "none"):
+        c = Case("autograd", 300, 136, 1100, "bf16", 0.1, 0.8, 4.0, 1e-3, 0.1, red, weight_std=0.1, seed=17)
+        d = to_device(_inputs(c), c.dtype)
+        x = d["hidden"].clone().requires_grad_(True)
+        w = d["weight"].clone().requires_grad_(True)
+        b = d["bias"].clone().requires_grad_(True)
+        loss = flce_lib.linear_cross_entropy(x, w, d["targets"], b, **_opts(c))
+        up = torch.full((), 2.5, device="cuda") if red == "sum" else torch.linspace(-1, 1, c.n, device="cuda")
+        (loss * up).sum().backward()
+        l2, lse, _ = flce_lib.forward(d["hidden"], d["weight"], d["targets"], d["bias"], **_opts(c))
+        g = up.reshape(1) if red == "sum" else up
+        gh, gw, gb = flce_lib.backward(d["hidden"], d["weight"], d["targets"], lse, g.float().contiguous(),
+                                       d["bias"], **_opts(c))
+        torch.cuda.synchronize()
+        assert torch.equal(loss.detach(), l2)
+        assert torch.equal(x.grad, gh) and torch.equal(w.grad, gw) and torch.equal(b.grad, gb)
