@@ -139,7 +139,8 @@ def test_forward_backward_f16_small_gradients(flce_lib):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["bf16_n8192_h4096_v128256", "bf16_n16384_h2048_v256000"])
+@pytest.mark.parametrize("name", ["bf16_n8192_h4096_v128256", "bf16_n16384_h2048_v256000",
+                                  "bf16_n8192_h4096_v32000_zipf", "f16_n8192_h4096_v128256"])
 def test_forward_backward_full_size_sampled(flce_lib, name):
     _sampled_check(flce_lib, si.WORKLOADS[name], run=lambda f, c, d: _run_fused(f, c, d, 0))
 
