@@ -182,6 +182,20 @@ int flce_forward_backward(const flce_params* p, int64_t block_rows, const void* 
                           void* grad_bias, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Multiplies the gradients flce_forward_backward wrote, in place, by the device
+ * fp32 scalar g: the upstream gradient of a "sum" or "mean" loss that arrives
+ * after the call (which then ran with grad_loss = 1), as the chunked pages do it
+ * ("Chunked Linear Loss" page, "Gradient handling": gradients precomputed in
+ * the forward pass, scaled by the upstream scalar in the backward).
+ * grad_hidden (N x H, params->dtype), grad_weight (V x H,
+ * params->grad_weight_dtype), grad_bias (V, params->dtype) or NULL; each
+ * element is rounded once more to its dtype.  g == 1 changes nothing.  Not for
+ * "none" (the per-row upstream gradient must go into flce_forward_backward).
+ */
+int flce_scale_gradients(const flce_params* p, const float* g, void* grad_hidden, void* grad_weight,
+                         void* grad_bias, void* stream);
+
+/*
  * Synchronises `stream`, then reads the status word that the last forward,
  * backward or forward-backward call on this workspace left: FLCE_OK, FLCE_ERR_TARGET_OUT_OF_RANGE,
  * or FLCE_ERR_HIP if the stream reports an error.

@@ -47,7 +47,7 @@ FLCE_GRAD_WEIGHT_ACCUM_IN_OUTPUT = 8
 EXPORTED = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_get_status",
             "flce_status_string", "flce_version", "flce_chunked_workspace_size",
             "flce_chunked_linear_loss", "flce_weighted_mse_chunk", "flce_forward_backward_workspace_size",
-            "flce_forward_backward")
+            "flce_forward_backward", "flce_scale_gradients")
 
 
 class flce_params(ctypes.Structure):
@@ -138,6 +138,8 @@ def load(path: Optional[str] = None):
     lib.flce_forward_backward_workspace_size.restype = ctypes.c_int
     lib.flce_forward_backward.argtypes = [P, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.flce_forward_backward.restype = ctypes.c_int
+    lib.flce_scale_gradients.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.flce_scale_gradients.restype = ctypes.c_int
     CP = ctypes.POINTER(flce_chunked_params)
     lib.flce_chunked_workspace_size.argtypes = [CP, ctypes.POINTER(sz)]
     lib.flce_chunked_workspace_size.restype = ctypes.c_int
@@ -187,6 +189,10 @@ def flce_forward_backward(params, block_rows, hidden, weight, bias, targets, gra
     return load().flce_forward_backward(ctypes.byref(params), block_rows, hidden, weight, bias, targets, grad_loss,
                                         loss, lse, num_correct, entropy_sum, grad_hidden, grad_weight, grad_bias,
                                         workspace, workspace_bytes, stream)
+
+
+def flce_scale_gradients(params, g, grad_hidden, grad_weight, grad_bias, stream) -> int:
+    return load().flce_scale_gradients(ctypes.byref(params), g, grad_hidden, grad_weight, grad_bias, stream)
 
 
 def flce_chunked_workspace_size(params: flce_chunked_params) -> int:
@@ -413,15 +419,46 @@ def forward_backward(hidden, weight, targets, grad_loss, bias=None, *, logit_sca
 
 def linear_cross_entropy(hidden, weight, targets, bias=None, *, logit_scale: float = 1.0,
                          softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
-                         reduction: str = "mean"):
-    """The loss as a differentiable torch op: flce_forward now, flce_backward (which recomputes
-    the logit tiles from hidden, weight and the saved LSE) when autograd asks for gradients,
-    with the upstream gradient autograd supplies.  Returns the loss (a scalar, or (N,) for
-    "none")."""
+                         reduction: str = "mean", one_pass: bool = False):
+    """The loss as a differentiable torch op.  Returns the loss (a scalar, or (N,) for "none").
+
+    one_pass=False: flce_forward now, flce_backward (which recomputes the logit tiles from
+    hidden, weight and the saved LSE) when autograd asks for gradients, with the upstream
+    gradient autograd supplies.
+    one_pass=True ("sum" / "mean" only): flce_forward_backward now, with an upstream gradient
+    of 1, keeping the gradients; autograd's backward multiplies them by the upstream scalar
+    (flce_scale_gradients), once: the graph cannot be backpropagated a second time."""
     import torch
 
     opts = dict(logit_scale=logit_scale, softcap=softcap, z_loss=z_loss, ignore_index=ignore_index,
                 reduction=reduction)
+    if one_pass:
+        if reduction == "none":
+            raise ValueError('one_pass needs reduction "sum" or "mean": the per-row upstream gradient of '
+                             '"none" must be known before the pass (use forward_backward)')
+
+        class _OnePass(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, x, w, b):
+                one = torch.ones(1, dtype=torch.float32, device=x.device)
+                loss, _, _, gh, gw, gb = forward_backward(x, w, targets, one, b, **opts)
+                p = make_params(x.shape[0], x.shape[1], w.shape[0], dtype=_dtype_name(x), **opts)
+                ctx.state = [p, gh, gw, gb]
+                return loss
+
+            @staticmethod
+            def backward(ctx, g):
+                if ctx.state is None:
+                    raise RuntimeError("the one-pass linear_cross_entropy gradients were already used")
+                p, gh, gw, gb = ctx.state
+                ctx.state = None
+                g = g.detach().to(torch.float32).contiguous().reshape(1)
+                rc = flce_scale_gradients(p, _ptr(g), _ptr(gh), _ptr(gw), _ptr(gb), _stream_handle(g.device))
+                if rc != FLCE_OK:
+                    raise FlceError(rc, "flce_scale_gradients")
+                return gh, gw, gb
+
+        return _OnePass.apply(hidden, weight, bias)
 
     class _Fn(torch.autograd.Function):
         @staticmethod

@@ -385,6 +385,19 @@ int flce_forward_backward(const flce_params* p, int64_t block_rows, const void* 
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
+int flce_scale_gradients(const flce_params* p, const float* g, void* grad_hidden, void* grad_weight,
+                         void* grad_bias, void* stream) {
+  Plan pl;
+  const int rc = make_plan(p, &pl);
+  if (rc != FLCE_OK) return rc;
+  if (pl.reduction == FLCE_REDUCTION_NONE || !g || !grad_weight) return FLCE_ERR_INVALID_ARG;
+  if (pl.N > 0 && !grad_hidden) return FLCE_ERR_INVALID_ARG;
+  if (!aligned16(grad_hidden) || !aligned16(grad_weight) || !aligned16(grad_bias)) return FLCE_ERR_UNSUPPORTED;
+  const hipError_t e = launch_scale_gradients(pl, g, grad_hidden, grad_weight, grad_bias,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
 int flce_chunked_workspace_size(const flce_chunked_params* p, size_t* bytes) {
   if (!bytes) return FLCE_ERR_INVALID_ARG;
   ChunkPlan pl;

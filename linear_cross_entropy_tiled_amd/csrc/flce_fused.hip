@@ -252,4 +252,40 @@ hipError_t launch_forward_backward(const Plan& pl, const void* hidden, const voi
   return hipGetLastError();
 }
 
+// In-place x *= g over n elements of type T, four per thread step; all threads
+// return at once when g == 1.
+template <typename T>
+__global__ __launch_bounds__(256) void scale_kernel(T* x, int64_t n, const float* g) {
+  typedef typename Quad<T>::type Q;
+  const float s = g[0];
+  if (s == 1.0f) return;
+  const int64_t n4 = n / 4;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    Q v = reinterpret_cast<Q*>(x)[i];
+#pragma unroll
+    for (int j = 0; j < 4; j++) v[j] = (T)((float)v[j] * s);
+    reinterpret_cast<Q*>(x)[i] = v;
+  }
+  for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) x[i] = (T)((float)x[i] * s);
+}
+
+static void launch_scale(int dtype, void* x, int64_t n, const float* g, hipStream_t st) {
+  if (n <= 0) return;
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  if (dtype == FLCE_BF16) scale_kernel<bf16><<<(int)blocks, 256, 0, st>>>(reinterpret_cast<bf16*>(x), n, g);
+  else if (dtype == FLCE_F16) scale_kernel<f16><<<(int)blocks, 256, 0, st>>>(reinterpret_cast<f16*>(x), n, g);
+  else scale_kernel<float><<<(int)blocks, 256, 0, st>>>(reinterpret_cast<float*>(x), n, g);
+}
+
+hipError_t launch_scale_gradients(const Plan& pl, const float* g, void* grad_hidden, void* grad_weight,
+                                  void* grad_bias, hipStream_t st) {
+  launch_scale(pl.dtype, grad_hidden, pl.N * pl.H, g, st);
+  launch_scale(pl.gw_dtype, grad_weight, pl.V * pl.H, g, st);
+  if (grad_bias) launch_scale(pl.dtype, grad_bias, pl.V, g, st);
+  return hipGetLastError();
+}
+
 }  // namespace flce

@@ -161,6 +161,9 @@ hipError_t launch_forward_backward(const Plan& pl, const void* hidden, const voi
                                    int64_t* num_correct, float* entropy_sum, void* grad_hidden, void* grad_weight,
                                    void* grad_bias, char* ws, hipStream_t st);
 
+hipError_t launch_scale_gradients(const Plan& pl, const float* g, void* grad_hidden, void* grad_weight,
+                                  void* grad_bias, hipStream_t st);
+
 hipError_t launch_forward(const Plan& pl, const void* hidden, const void* weight, const void* bias,
                           const void* targets, float* loss, float* lse, int64_t* num_correct,
                           float* entropy_sum, char* ws, hipStream_t st);

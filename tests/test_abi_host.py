@@ -193,3 +193,12 @@ def test_forward_backward_workspace_and_validation(lib):
     assert call(gb=16) == flce.FLCE_ERR_INVALID_ARG          # grad_bias without bias
     assert call(hidden=18) == flce.FLCE_ERR_UNSUPPORTED
     assert call(wsb=8) == flce.FLCE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_scale_gradients_validation(lib):
+    p = flce.make_params(64, 64, 100, reduction="sum")
+    assert lib.flce_scale_gradients(ctypes.byref(p), None, 16, 16, None, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_scale_gradients(ctypes.byref(p), 16, 16, None, None, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_scale_gradients(ctypes.byref(p), 16, 18, 16, None, None) == flce.FLCE_ERR_UNSUPPORTED
+    pn = flce.make_params(64, 64, 100, reduction="none")
+    assert lib.flce_scale_gradients(ctypes.byref(pn), 16, 16, 16, None, None) == flce.FLCE_ERR_INVALID_ARG

@@ -414,3 +414,35 @@ def test_autograd_function(flce_lib):
         torch.cuda.synchronize()
         assert torch.equal(loss.detach(), l2)
         assert torch.equal(x.grad, gh) and torch.equal(w.grad, gw) and torch.equal(b.grad, gb)
+
+
+def test_autograd_one_pass(flce_lib):
+    """linear_cross_entropy(one_pass=True): gradients precomputed with an upstream gradient of 1,
+    scaled in backward by the one autograd passes (2.5 here, and 1); they match the two-call op's
+    within the gradient tolerance; "none" is refused, and so is a second backward."""
+    import torch
+    for red, up in (("sum", 2.5), ("mean", 1.0)):
+        c = Case("autograd_one_pass", 700, 136, 1100, "bf16", 0.1, 0.8, 4.0, 1e-3, 0.1, red, weight_std=0.1, seed=19)
+        d = to_device(_inputs(c), c.dtype)
+        grads = []
+        for one_pass in (False, True):
+            x = d["hidden"].clone().requires_grad_(True)
+            w = d["weight"].clone().requires_grad_(True)
+            b = d["bias"].clone().requires_grad_(True)
+            loss = flce_lib.linear_cross_entropy(x, w, d["targets"], b, one_pass=one_pass, **_opts(c))
+            (loss * up).backward()
+            torch.cuda.synchronize()
+            grads.append((loss.detach(), x.grad, w.grad, b.grad))
+        (l0, *g0), (l1, *g1) = grads
+        assert abs(l0.item() - l1.item()) <= 1e-5 * abs(l0.item())
+        for name, a, r in zip(("grad_hidden", "grad_weight", "grad_bias"), g1, g0):
+            assert_grad_close(t2np(a), t2np(r), name)
+    c = Case("autograd_one_pass_none", 300, 64, 500, "bf16", reduction="none", weight_std=0.1)
+    d = to_device(_inputs(c), c.dtype)
+    with pytest.raises(ValueError):
+        flce_lib.linear_cross_entropy(d["hidden"], d["weight"], d["targets"], reduction="none", one_pass=True)
+    x = d["hidden"].clone().requires_grad_(True)
+    loss = flce_lib.linear_cross_entropy(x, d["weight"], d["targets"], reduction="sum", one_pass=True)
+    loss.backward(retain_graph=True)
+    with pytest.raises(RuntimeError):
+        loss.backward()
