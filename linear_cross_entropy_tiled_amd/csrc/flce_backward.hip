@@ -393,35 +393,52 @@ __device__ __forceinline__ void block_store_t(float* acc32, OutT* out, int ld,
                                               int lane) {
   constexpr bool READ_ACC = MODE == 1 || MODE == 2;
   constexpr bool READ_OUT = ACC && MODE >= 2;
+  // The accumulator holds, per lane, 4 consecutive columns of one row (32 rows
+  // per store instruction, 16 bytes each).  It goes through a 16 KiB LDS
+  // region of this wave's own, one 32-row MFMA tile column at a time, and
+  // leaves as whole rows: two 128-column rows per instruction, every cache
+  // line written whole.  Rows are 512 bytes; the 16-byte chunk c of row r sits
+  // at chunk c ^ r, so both the scattered writes and the row reads are free of
+  // bank conflicts.  Every LDS read of the main loop whose value is used has
+  // completed before it returns, and a wave reads back only what it wrote.
+  char* stage = g_lds + (threadIdx.x >> 6) * 16384;
+  const int r_w = lane & 31;
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
-    const size_t row = (size_t)(rbase + ni * 32 + (lane & 31)) * ld + cbase + 4 * (lane >> 5);
 #pragma unroll
-    for (int m0 = 0; m0 < kMI; m0 += 2) {
-      f32x4 pa[2][4], po[2][4];
+    for (int mi = 0; mi < kMI; mi++)
 #pragma unroll
-      for (int mi = 0; mi < 2; mi++)
+      for (int g = 0; g < 4; g++) {
+        const int ch = mi * 8 + 2 * g + (lane >> 5);
+        *reinterpret_cast<f32x4*>(stage + r_w * 512 + ((ch ^ r_w) << 4)) =
+            f32x4{acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]};
+      }
+    const int c = lane & 31;
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-          const size_t o = row + (m0 + mi) * 32 + 8 * g;
-          if constexpr (READ_ACC) pa[mi][g] = *reinterpret_cast<const f32x4*>(acc32 + o);
-          if constexpr (READ_OUT) po[mi][g] = load4v<OutT>(out + o);
+    for (int k0 = 0; k0 < 16; k0 += 4) {
+      f32x4 pa[4], po[4], cv[4];
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const int rr = 2 * (k0 + k) + (lane >> 5);
+        const size_t o = (size_t)(rbase + ni * 32 + rr) * ld + cbase + 4 * c;
+        if constexpr (READ_ACC) pa[k] = *reinterpret_cast<const f32x4*>(acc32 + o);
+        if constexpr (READ_OUT) po[k] = load4v<OutT>(out + o);
+        cv[k] = *reinterpret_cast<const f32x4*>(stage + rr * 512 + ((c ^ rr) << 4));
+      }
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const int rr = 2 * (k0 + k) + (lane >> 5);
+        const size_t o = (size_t)(rbase + ni * 32 + rr) * ld + cbase + 4 * c;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          v[j] = cv[k][j] * inv;
+          if constexpr (READ_ACC) v[j] += pa[k][j];
+          if constexpr (READ_OUT) v[j] += po[k][j];
         }
-#pragma unroll
-      for (int mi = 0; mi < 2; mi++)
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-          const size_t o = row + (m0 + mi) * 32 + 8 * g;
-          float c[4];
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            c[j] = acc[m0 + mi][ni][4 * g + j] * inv;
-            if constexpr (READ_ACC) c[j] += pa[mi][g][j];
-            if constexpr (READ_OUT) c[j] += po[mi][g][j];
-          }
-          if constexpr (MODE <= 1) store4(acc32 + o, c[0], c[1], c[2], c[3]);
-          else store4(out + o, c[0], c[1], c[2], c[3]);
-        }
+        if constexpr (MODE <= 1) store4(acc32 + o, v[0], v[1], v[2], v[3]);
+        else store4(out + o, v[0], v[1], v[2], v[3]);
+      }
     }
   }
 }
