@@ -194,14 +194,33 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
           if constexpr (SOFTCAP) rr[r] = fast_rcp(fast_exp2(u[r]) + 1.0f);
         }
         if constexpr (STORE_Z) {
-          const int t = wn * kWaveN + ni * 32 + (lane & 31);   // within this token tile
-          T* zrow = reinterpret_cast<T*>(a.z) + (size_t)(t0 + t) * a.ldz + vw + mi * 32 + 4 * (lane >> 5);
+          if constexpr (sizeof(T) == 2) {
+            // into this wave's 16 KiB of LDS: 64 token rows x 128 logits (256 B);
+            // 16-byte chunk q of row t sits at chunk q ^ (t & 15)
+            const int tl = ni * 32 + (lane & 31);
+            // (opaque, so that the swizzled offsets are formed here and not
+            // kept in registers across the main loop)
+            int key = (tl & 15) << 4;
+            asm volatile("" : "+v"(key));
+            char* zst = g_lds + wave * 16384 + tl * 256 + 8 * (lane >> 5);
 #pragma unroll
-          for (int g = 0; g < 4; g++) {
-            float z4[4];
+            for (int g = 0; g < 4; g++) {
+              float z4[4];
 #pragma unroll
-            for (int j = 0; j < 4; j++) z4[j] = SOFTCAP ? fmaf(-a.two_cap, rr[4 * g + j], a.cap) : u[4 * g + j];
-            store_z4(zrow + 8 * g, z4);
+              for (int j = 0; j < 4; j++) z4[j] = SOFTCAP ? fmaf(-a.two_cap, rr[4 * g + j], a.cap) : u[4 * g + j];
+              const int q = mi * 4 + g;   // logits mi*32 + 8g + 4*(lane/32) .. +3
+              store_z4(reinterpret_cast<T*>(zst + ((q << 4) ^ key)), z4);
+            }
+          } else {
+            const int t = wn * kWaveN + ni * 32 + (lane & 31);   // within this token tile
+            T* zrow = reinterpret_cast<T*>(a.z) + (size_t)(t0 + t) * a.ldz + vw + mi * 32 + 4 * (lane >> 5);
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+              float z4[4];
+#pragma unroll
+              for (int j = 0; j < 4; j++) z4[j] = SOFTCAP ? fmaf(-a.two_cap, rr[4 * g + j], a.cap) : u[4 * g + j];
+              store_z4(zrow + 8 * g, z4);
+            }
           }
         }
         if (ragged) {
@@ -267,6 +286,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
         st[ni].T = fmaf(st[ni].T, alpha, sz);
         st[ni].m = m_new;
       }
+    }
+    if constexpr (STORE_Z && sizeof(T) == 2) {
+      // the staged logits leave as whole rows, four 256-byte rows per store
+      // instruction; then every wave has read its region back before the next
+      // tile's first stage is loaded over it
+      const char* zst = g_lds + wave * 16384;
+      const int q = lane & 15;
+      T* zbase = reinterpret_cast<T*>(a.z) + (size_t)(t0 + wn * kWaveN + (lane >> 4)) * a.ldz + vw + 8 * q;
+#pragma unroll 2
+      for (int k = 0; k < 16; k++) {
+        const int r = 4 * k + (lane >> 4);
+        const i32x4 v = *reinterpret_cast<const i32x4*>(zst + r * 256 + ((q ^ (r & 15)) << 4));
+        *reinterpret_cast<i32x4*>(zbase + (size_t)(4 * k) * a.ldz) = v;
+      }
+      __syncthreads();
     }
   }
 
