@@ -322,10 +322,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
       }
 #pragma unroll
       for (int r = 0; r < 16; r++) cs[r] += d[r];
-      const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
-      T* drow = D + (size_t)t * a.ldD + (vw - a.cv0) + mi * 32 + 4 * (lane >> 5);
+      if constexpr (sizeof(T) == 2) {
+        // into this wave's 16 KiB of LDS (64 token rows x 128 logits; 16-byte
+        // chunk q of row t at chunk q ^ (t & 15)), stored as whole rows below;
+        // the key is opaque so that the offsets are not held across the main loop
+        const int tl = ni * 32 + (lane & 31);
+        int key = (tl & 15) << 4;
+        asm volatile("" : "+v"(key));
+        char* dst = g_lds + wave * 16384 + tl * 256 + 8 * (lane >> 5);
 #pragma unroll
-      for (int g = 0; g < 4; g++) store4(drow + 8 * g, d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]);
+        for (int g = 0; g < 4; g++)
+          store4(reinterpret_cast<T*>(dst + (((mi * 4 + g) << 4) ^ key)), d[4 * g], d[4 * g + 1], d[4 * g + 2],
+                 d[4 * g + 3]);
+      } else {
+        const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
+        T* drow = D + (size_t)t * a.ldD + (vw - a.cv0) + mi * 32 + 4 * (lane >> 5);
+#pragma unroll
+        for (int g = 0; g < 4; g++) store4(drow + 8 * g, d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]);
+      }
     }
     if constexpr (HAS_BIAS) {
       // reduce-scatter the 16 column sums over the 32 lanes of each half;
@@ -342,6 +356,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
       }
       gsum[mi] = cs[0] + __shfl_xor(cs[0], 1);
     }
+  }
+  if constexpr (sizeof(T) == 2) {
+    // the staged logit gradient leaves as whole rows, four 256-byte rows per
+    // store instruction
+    const char* src = g_lds + wave * 16384;
+    const int q = lane & 15;
+    T* dbase = D + (size_t)(t0 + wn * kWaveN + (lane >> 4)) * a.ldD + (vw - a.cv0) + 8 * q;
+#pragma unroll 2
+    for (int k = 0; k < 16; k++) {
+      const int r = 4 * k + (lane >> 4);
+      const i32x4 v = *reinterpret_cast<const i32x4*>(src + r * 256 + ((q ^ (r & 15)) << 4));
+      *reinterpret_cast<i32x4*>(dbase + (size_t)(4 * k) * a.ldD) = v;
+    }
+    // the column sums below go through LDS over the staging areas
+    if constexpr (HAS_BIAS) __syncthreads();
   }
   if constexpr (HAS_BIAS) {
     // the kWavesN waves with the same wm hold the same vocabulary rows:
