@@ -10,7 +10,7 @@ import pytest
 import oracle
 import synth_inputs as si
 from gpu_helpers import assert_grad_close, assert_loss_close, assert_num_correct, t2np, to_device, widened
-from test_gpu_parity import SMALL_CASES, Case, _inputs, _opts, _sampled_check, _say
+from test_gpu_parity import RAGGED_MID, SMALL_CASES, Case, _inputs, _opts, _sampled_check, _say
 
 pytestmark = pytest.mark.gpu
 
@@ -187,3 +187,10 @@ def test_forward_backward_grad_weight_accumulated_in_weight_dtype(flce_lib):
     out_f = _run_fused(flce_lib, c, d, 256)
     assert torch.equal(out_w[3], out_f[3])            # grad_hidden does not depend on it
     assert not torch.equal(out_w[4], out_f[4])
+
+
+@pytest.mark.slow
+def test_forward_backward_ragged_mid_size_sampled(flce_lib):
+    """N=6000, H=1600, V=50257, every option on, in blocks of 2048 rows: three blocks, the last
+    ragged, the fp32 grad_weight partial carried across them."""
+    _sampled_check(flce_lib, RAGGED_MID, run=lambda f, c, d: _run_fused(f, c, d, 2048))
