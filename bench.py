@@ -1,6 +1,7 @@
 """Benchmark: fused linear cross-entropy forward + backward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path both|fused|split]
+                    [--block-rows R] [--grad-weight-accum fp32|weight] [--no-cpu-baseline]
 
 One step is a full forward + backward (loss, LSE, metrics, grad_hidden,
 grad_weight, grad_bias) on the headline workload: N=8192 tokens, H=4096,
