@@ -84,13 +84,14 @@ class ForwardResult:
     row_loss: np.ndarray        # (N,) per-row loss, 0 on ignored rows
     lse: np.ndarray             # (N,) log-sum-exp of z, every row
     argmax: np.ndarray          # (N,) lowest index of the row maximum
-    top2_gap: np.ndarray        # (N,) largest minus second-largest z
+    top2_gap: np.ndarray        # (N,) largest minus second-largest z (0 on a tie, inf if V = 1)
     entropy: np.ndarray         # (N,) softmax entropy in nats, every row
     target_logit: np.ndarray    # (N,) z at the target, NaN on ignored rows
     valid: np.ndarray           # (N,) bool
     n_valid: int
     num_correct: int
     entropy_sum: float
+    row_max: np.ndarray         # (N,) the row maximum of z (the value at argmax)
 
 
 def forward(hidden, weight, bias, targets, *, logit_scale=1.0, softcap=None,
@@ -111,11 +112,13 @@ def forward(hidden, weight, bias, targets, *, logit_scale=1.0, softcap=None,
     gap = np.full(n, np.inf)
     ent = np.zeros(n)
     zt = np.full(n, np.nan)
+    zmax = np.zeros(n)
     rb = row_block or _row_block(n, vocab)
     for r0 in range(0, n, rb):
         r1 = min(n, r0 + rb)
         z = _logits_block(hidden[r0:r1], weight, bias, logit_scale, softcap)
         m = z.max(axis=1)
+        zmax[r0:r1] = m
         e = np.exp(z - m[:, None])
         s = e.sum(axis=1)
         lse[r0:r1] = m + np.log(s)
@@ -138,7 +141,7 @@ def forward(hidden, weight, bias, targets, *, logit_scale=1.0, softcap=None,
     num_correct = int((valid & (argmax == targets)).sum())
     entropy_sum = float(ent[valid].sum())
     return ForwardResult(loss, row_loss, lse, argmax, gap, ent, zt, valid, n_valid,
-                         num_correct, entropy_sum)
+                         num_correct, entropy_sum, zmax)
 
 
 def row_coefficients(targets, grad_loss, *, ignore_index=-100, reduction="mean"):
@@ -251,12 +254,14 @@ def full_pass_with_bias_grad(hidden, weight, bias, targets, grad_loss, *, logit_
     gap = np.full(n, np.inf)
     ent = np.zeros(n)
     zt = np.full(n, np.nan)
+    zmax = np.zeros(n)
     gb = np.zeros(vocab)
     rb = row_block or _row_block(n, vocab)
     for r0 in range(0, n, rb):
         r1 = min(n, r0 + rb)
         z = _logits_block(hidden[r0:r1], weight, bias, logit_scale, softcap)
         m = z.max(axis=1)
+        zmax[r0:r1] = m
         e = np.exp(z - m[:, None])
         s = e.sum(axis=1)
         lse_b = m + np.log(s)
@@ -284,5 +289,5 @@ def full_pass_with_bias_grad(hidden, weight, bias, targets, grad_loss, *, logit_
         loss = np.array(row_loss.sum() / n_valid if n_valid else math.nan)
     num_correct = int((valid & (argmax == targets)).sum())
     fwd = ForwardResult(loss, row_loss, lse, argmax, gap, ent, zt, valid, n_valid,
-                        num_correct, float(ent[valid].sum()))
+                        num_correct, float(ent[valid].sum()), zmax)
     return fwd, gb

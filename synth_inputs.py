@@ -129,19 +129,48 @@ def _targets(rng: np.random.Generator, n: int, vocab: int, kind: str, zipf_s: fl
     raise ValueError(kind)
 
 
+def _round_to(x64: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = np.ascontiguousarray(x64, dtype=np.float32)
+    if dtype == "bf16":
+        return round_to_bf16_bits(x32)
+    if dtype == "f16":
+        return x32.astype(np.float16)
+    return x32
+
+
+def _plant(hidden: np.ndarray, weight: np.ndarray, t: np.ndarray, rows: np.ndarray, margin: float,
+           dtype: str) -> None:
+    """hidden[i] += margin * W[t_i] / |W[t_i]|^2 on the given rows, rounded back to the
+    input type: the row's dot product with W[t_i] grows by about `margin` while its dot
+    products with the other (nearly orthogonal) weight rows barely move.  Input
+    construction only: the hidden rows of a batch whose targets are often its best match."""
+    for r0 in range(0, rows.size, 4096):
+        rr = rows[r0:r0 + 4096]
+        w = widen(weight[t[rr]], dtype)
+        x = widen(hidden[rr], dtype)
+        x += margin * w / np.maximum((w * w).sum(axis=1, keepdims=True), 1e-30)
+        hidden[rr] = _round_to(x, dtype)
+
+
 def make_inputs(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
                 weight_std: float = 0.02, hidden_std: float = 1.0,
                 bias_std: Optional[float] = None, targets: str = "uniform",
                 zipf_s: float = 1.1, ignore_frac: float = 0.0,
-                reduction: str = "mean", seed: int = 0) -> dict:
+                reduction: str = "mean", seed: int = 0, plant_frac: float = 0.0,
+                plant_margin: float = 8.0) -> dict:
     """Draw one problem.  Returns numpy arrays:
 
     hidden (N,H), weight (V,H), bias (V,) or None -- uint16 bf16 patterns, float16 or float32;
     targets (N,) int64 with exactly floor(ignore_frac*N) entries set to -100;
     grad_loss: float32 scalar 1.0 for sum/mean, (N,) N(0,1) for "none".
+
+    plant_frac > 0: a seeded floor(plant_frac*N) of the rows get a component
+    along their target's weight row (``_plant``, `plant_margin` in units of the
+    raw dot product), so that the target is usually the row's largest logit and
+    the argmax count is far from zero.  The other streams are unchanged.
     """
     ss = np.random.SeedSequence(seed)
-    s_h, s_w, s_b, s_t, s_i, s_g = ss.spawn(6)
+    s_h, s_w, s_b, s_t, s_i, s_g, s_p = ss.spawn(7)
     out = {
         "hidden": _normal(np.random.Generator(np.random.PCG64(s_h)), (n_tokens, hidden), hidden_std, dtype),
         "weight": _normal(np.random.Generator(np.random.PCG64(s_w)), (vocab, hidden), weight_std, dtype),
@@ -149,6 +178,10 @@ def make_inputs(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
                  _normal(np.random.Generator(np.random.PCG64(s_b)), (vocab,), bias_std, dtype)),
     }
     t = _targets(np.random.Generator(np.random.PCG64(s_t)), n_tokens, vocab, targets, zipf_s)
+    n_plant = int(np.floor(plant_frac * n_tokens))
+    if n_plant:
+        rows = np.sort(np.random.Generator(np.random.PCG64(s_p)).permutation(n_tokens)[:n_plant])
+        _plant(out["hidden"], out["weight"], t, rows, plant_margin, dtype)
     n_ign = int(np.floor(ignore_frac * n_tokens))
     if n_ign:
         perm = np.random.Generator(np.random.PCG64(s_i)).permutation(n_tokens)

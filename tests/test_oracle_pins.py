@@ -134,6 +134,63 @@ def test_argmax_ties_lowest_index():
         assert fwd.argmax[i] == best
 
 
+def _identity_problem(rows):
+    """Logits equal to the given rows: H = V, W = I, x = rows (so x.W^T = x exactly)."""
+    x = np.asarray(rows, dtype=np.float64)
+    v = x.shape[1]
+    return x, np.eye(v), np.zeros(x.shape[0], dtype=np.int64)
+
+
+@pytest.mark.parametrize("fn", ["forward", "full_pass_with_bias_grad"])
+def test_top2_gap_and_row_max_closed_forms(fn):
+    """top2_gap is the largest minus the second-largest logit of the row (0 on a
+    tie), row_max the largest; rows chosen so both are exact binary fractions."""
+    x, w, t = _identity_problem([[3.0, 1.0, 2.0],        # gap 1 (not 2: the runner-up is 2)
+                                 [1.0, 3.0, 3.0],        # tie at the top: gap 0, argmax 1
+                                 [-5.0, 2.0, 1.75],      # gap 0.25
+                                 [0.5, 0.5, 0.5],        # all equal: gap 0, argmax 0
+                                 [-1.0, -4.0, -0.5]])    # negative logits: gap 0.5
+    if fn == "forward":
+        fwd = oracle.forward(x, w, None, t, reduction="sum")
+    else:
+        fwd, _ = oracle.full_pass_with_bias_grad(x, w, None, t, np.array(1.0), reduction="sum")
+    assert list(fwd.top2_gap) == [1.0, 0.0, 0.25, 0.0, 0.5]
+    assert list(fwd.row_max) == [3.0, 3.0, 2.0, 0.5, -0.5]
+    assert list(fwd.argmax) == [0, 1, 1, 0, 2]
+
+
+def test_top2_gap_single_column_is_inf():
+    x, w, t = _identity_problem([[0.25], [-7.0]])
+    fwd = oracle.forward(x, w, None, t, reduction="sum")
+    assert np.isinf(fwd.top2_gap).all() and (fwd.top2_gap > 0).all()
+    assert list(fwd.row_max) == [0.25, -7.0]
+
+
+def test_top2_gap_and_row_max_follow_the_transformed_logits():
+    """Scale and cap apply before the metrics: with s = 2, cap = 3 the row
+    u = (1, 0.5, -1) has z = 3 tanh(2u/3); with s = -1 the order reverses."""
+    x, w, t = _identity_problem([[1.0, 0.5, -1.0]])
+    fwd = oracle.forward(x, w, None, t, logit_scale=2.0, softcap=3.0, reduction="sum")
+    assert fwd.row_max[0] == pytest.approx(3 * math.tanh(2 / 3), rel=1e-15)
+    assert fwd.top2_gap[0] == pytest.approx(3 * (math.tanh(2 / 3) - math.tanh(1 / 3)), rel=1e-14)
+    x, w, t = _identity_problem([[3.0, 1.0, 2.0]])
+    fwd = oracle.forward(x, w, None, t, logit_scale=-1.0, reduction="sum")
+    assert fwd.argmax[0] == 1 and fwd.row_max[0] == -1.0 and fwd.top2_gap[0] == 1.0
+
+
+def test_row_max_against_brute_force():
+    """Random rows: row_max and top2_gap equal a sort of the row's z, argmax its first maximum."""
+    x, w, b, t = _problem(9, 4, 13, seed=8)
+    fwd = oracle.forward(x, w, b, t, logit_scale=0.7, softcap=2.0, reduction="sum")
+    for i in range(9):
+        z = [2.0 * math.tanh(0.7 * (sum(x[i, k] * w[j, k] for k in range(4)) + b[j]) / 2.0)
+             for j in range(13)]
+        zs = sorted(z)
+        assert fwd.row_max[i] == pytest.approx(zs[-1], rel=1e-13)
+        assert fwd.top2_gap[i] == pytest.approx(zs[-1] - zs[-2], abs=1e-13)
+        assert fwd.argmax[i] == z.index(zs[-1])
+
+
 # ---------------------------------------------------------------- library special case
 
 @pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
