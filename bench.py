@@ -1,23 +1,25 @@
 """Benchmark: fused linear cross-entropy forward + backward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path both|fused|split]
-                    [--block-rows R] [--grad-weight-accum fp32|weight] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path split|both|fused]
+                    [--vocab-chunk C] [--block-rows R] [--grad-weight-accum fp32|weight] [--no-cpu-baseline]
 
 One step is a full forward + backward (loss, LSE, metrics, grad_hidden,
 grad_weight, grad_bias) on the headline workload: N=8192 tokens, H=4096,
 V=128256, bf16, bias, logit_scale 0.5, softcap 30, 5% ignored targets,
-reduction "sum".  Two implementations are timed: flce_forward_backward (one
-pass over row blocks, gradients from each block's stored logits: the headline
-`value`) and flce_forward followed by flce_backward (the backward recomputes
-the logit tiles: `split_path`).  Inputs are seeded synthetic data already
-resident in device memory; outputs and workspaces are allocated before timing.
+reduction "sum", through flce_forward then flce_backward (the backward
+recomputes the logit tiles: 8*N*H*V flop per step, the metric's count).
+Inputs are seeded synthetic data already resident in device memory; outputs
+and workspaces are allocated before timing.
 
-Prints one JSON line.  `value` is tokens/s for the whole step; `tflops` counts
-the metric's 8*N*H*V (forward logits, recomputed logits and the two gradient
-contractions) per step, `tflops_executed` the 6*N*H*V the one-pass step
-actually runs.  `roofline` reports the forward tile kernel, timed with HIP
-events on the stream it is launched on; `cpu_baseline` times the fp64 CPU
-oracle on a bounded slice of the same workload.
+Prints one JSON line.  `value` is tokens/s of the whole step (wall clock over
+the K timed steps, bracketed by device synchronizations); `tflops` counts
+8*N*H*V per step.  Inside the timed steps the two calls go through
+flce_forward_timed / flce_backward_timed, which record HIP events on the
+calls' stream around every matrix-core launch: `kernels` gives each kernel's
+time per step, and `roofline` reports the one with the largest share.
+`--path both` also times flce_forward_backward (one pass over row blocks, no
+recompute, 6*N*H*V flop) as the side object `one_pass`.  `cpu_baseline` times
+the fp64 CPU oracle on a bounded slice of the same workload.
 """
 from __future__ import annotations
 
@@ -54,10 +56,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the forward tile kernel, from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None if it is stale."""
-    path = os.path.join(PROFILES, f"traffic_fwd_tiles_{workload}.txt")
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel`, from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None if there is none or it is stale."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -65,7 +67,7 @@ def measured_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != kernel_source_hash():
+    if kv.get("source_hash") != kernel_source_hash() or kv.get("kernel") != kernel:
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -122,11 +124,14 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS) + sorted(si.WMSE_WORKLOADS))
-    ap.add_argument("--path", choices=("both", "split", "fused"), default="both",
-                    help="fused: flce_forward_backward (one pass: gradients from each row block's stored "
-                         "logits); split: flce_forward then flce_backward (the backward recomputes the logit "
-                         "tiles); both (default): the fused step is the headline, the split step is reported "
-                         "beside it")
+    ap.add_argument("--path", choices=("split", "both", "fused"), default="split",
+                    help="split (default): flce_forward then flce_backward (the backward recomputes the logit "
+                         "tiles), the measured step; both: also time flce_forward_backward (one pass: gradients "
+                         "from each row block's stored logits, 6NHV) as the side object one_pass; fused: only "
+                         "the one-pass step")
+    ap.add_argument("--vocab-chunk", type=int, default=0,
+                    help="flce_backward: vocabulary rows per logit-gradient chunk (multiple of 256; 0 = the "
+                         "library's choice)")
     ap.add_argument("--block-rows", type=int, default=0,
                     help="rows per block of flce_forward_backward (a multiple of 256; 0 = the library's choice)")
     ap.add_argument("--grad-weight-accum", choices=("fp32", "weight"), default="fp32",
@@ -155,7 +160,7 @@ def main():
     opts = dict(logit_scale=wl.logit_scale, softcap=wl.softcap, z_loss=wl.z_loss,
                 ignore_index=si.IGNORE_INDEX, reduction=wl.reduction)
     pf = flce.make_params(n, h, v, dtype=wl.dtype, grad_weight_dtype=wl.grad_weight_dtype,
-                          grad_weight_accum_dtype=args.grad_weight_accum, **opts)
+                          grad_weight_accum_dtype=args.grad_weight_accum, vocab_chunk=args.vocab_chunk, **opts)
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
     loss = torch.empty(n if wl.reduction == "none" else 1, dtype=torch.float32, device="cuda")
     lse = torch.empty(n, dtype=torch.float32, device="cuda")
@@ -184,9 +189,9 @@ def main():
                          device="cuda")
 
         def step():
-            rc = flce.flce_forward_backward(pf, args.block_rows, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]),
-                                            P(gl), P(loss), P(lse), P(nc), P(ent), P(gh), P(gw), P(gb), P(ws),
-                                            ws.numel(), sh)
+            rc = flce.flce_forward_backward(pf, args.block_rows, P(d["hidden"]), P(d["weight"]), P(d["bias"]),
+                                            P(d["targets"]), P(gl), P(loss), P(lse), P(nc), P(ent), P(gh), P(gw),
+                                            P(gb), P(ws), ws.numel(), sh)
             if rc:
                 raise flce.FlceError(rc, "flce_forward_backward")
 
@@ -202,104 +207,127 @@ def main():
         mem = torch.cuda.max_memory_allocated() / 2**30
         del ws
         torch.cuda.empty_cache()
-        return {"ms_per_step": step_ms, "value": n / (step_ms * 1e-3), "peak_mem_gib": mem,
-                "tflops_8nhv": flop8 / (step_ms * 1e-3) / 1e12,
-                "tflops_executed": 0.75 * flop8 / (step_ms * 1e-3) / 1e12}
+        # the one-pass step executes 6NHV: no recompute
+        flop6 = 0.75 * flop8
+        return {"path": "flce_forward_backward (one pass over row blocks, no recompute: 6NHV executed)",
+                "ms_per_step": step_ms, "value": n / (step_ms * 1e-3), "unit": "tokens/s", "peak_mem_gib": mem,
+                "tflops_executed": flop6 / (step_ms * 1e-3) / 1e12,
+                "frac_of_peak_executed": flop6 / (step_ms * 1e-3) / 1e12 / peak}
 
     def time_split():
         ws_f = torch.empty(flce.flce_workspace_size(pf, flce.FLCE_PASS_FORWARD), dtype=torch.uint8, device="cuda")
         ws_b = torch.empty(flce.flce_workspace_size(pf, flce.FLCE_PASS_BACKWARD), dtype=torch.uint8, device="cuda")
+        # one event pair per matrix-core launch: the forward tile kernel, then 3 per vocabulary
+        # chunk; the first warm-up step counts them (at most one chunk per 256 vocabulary rows)
+        probe = flce.LaunchTimer(capacity=1 + 3 * ((v + 255) // 256), stream=stream)
 
-        def fwd():
-            rc = flce.flce_forward(pf, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]), P(loss),
-                                   P(lse), P(nc), P(ent), P(ws_f), ws_f.numel(), sh)
+        def fwd(t):
+            rc = flce.flce_forward_timed(pf, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]),
+                                         P(loss), P(lse), P(nc), P(ent), P(ws_f), ws_f.numel(), sh, t)
             if rc:
                 raise flce.FlceError(rc, "flce_forward")
 
-        def bwd():
-            rc = flce.flce_backward(pf, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]), P(lse),
-                                    P(gl), P(gh), P(gw), P(gb), P(ws_b), ws_b.numel(), sh)
+        def bwd(t):
+            rc = flce.flce_backward_timed(pf, P(d["hidden"]), P(d["weight"]), P(d["bias"]), P(d["targets"]),
+                                          P(lse), P(gl), P(gh), P(gw), P(gb), P(ws_b), ws_b.numel(), sh, t)
             if rc:
                 raise flce.FlceError(rc, "flce_backward")
 
         torch.cuda.reset_peak_memory_stats()
-        for _ in range(args.warmup):
-            fwd()
-            bwd()
+        for i in range(max(args.warmup, 1)):
+            fwd(probe.c if i == 0 else None)
+            bwd(probe.c if i == 0 else None)
         torch.cuda.synchronize()
-        # HIP events on the stream the kernels run on bracket each call
+        timer = flce.LaunchTimer(capacity=args.steps * probe.c.count, stream=stream)
+        del probe
+        # HIP events on the stream the kernels run on bracket each call and each launch
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
                torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        timer.reset()
         t0 = time.perf_counter()
         for e0, e1, e2 in ev:
             e0.record(stream)
-            fwd()
+            fwd(timer.c)
             e1.record(stream)
-            bwd()
+            bwd(timer.c)
             e2.record(stream)
         torch.cuda.synchronize()
         step_ms = (time.perf_counter() - t0) / args.steps * 1e3
         fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
         bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+        launches = timer.durations()
         mem = torch.cuda.max_memory_allocated() / 2**30
         del ws_f, ws_b
         torch.cuda.empty_cache()
+        # every kernel of the four does 2NHV per step in total (the chunk kernels in
+        # launches of 2*N*H*(rows of the chunk))
+        kernels = {}
+        for name, ms in launches.items():
+            per_step = float(np.sum(ms)) / args.steps
+            kernels[name] = {"launches_per_step": len(ms) // args.steps, "ms_per_step": per_step,
+                             "mean_launch_ms": float(np.mean(ms)),
+                             "tflops": 0.25 * flop8 / (per_step * 1e-3) / 1e12,
+                             "share_of_step": per_step / step_ms}
         return {"ms_per_step": step_ms, "value": n / (step_ms * 1e-3), "peak_mem_gib": mem,
                 "tflops_8nhv": flop8 / (step_ms * 1e-3) / 1e12, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
                 "fwd_tflops": 0.25 * flop8 / (fwd_ms * 1e-3) / 1e12,
-                "bwd_tflops": 0.75 * flop8 / (bwd_ms * 1e-3) / 1e12}
+                "bwd_tflops": 0.75 * flop8 / (bwd_ms * 1e-3) / 1e12, "kernels": kernels}
 
-    fused = time_fused() if args.path in ("both", "fused") else None
     split = time_split() if args.path in ("both", "split") else None
-    head = fused if fused is not None else split
+    fused = time_fused() if args.path in ("both", "fused") else None
+    plan_chunks = None
+    if split is not None:
+        lk = split["kernels"].get("bwd_dlogits_kernel")
+        plan_chunks = lk["launches_per_step"] if lk else None
     cfg = {"workload": wl.name, "n_tokens": n, "hidden": h, "vocab": v, "bias": wl.bias_std is not None,
            "logit_scale": wl.logit_scale, "softcap": wl.softcap, "z_loss": wl.z_loss,
            "ignore_frac": wl.ignore_frac, "reduction": wl.reduction,
-           "grad_weight_dtype": wl.grad_weight_dtype or wl.dtype, "block_rows": args.block_rows or "library choice",
-           "grad_weight_accum_dtype": args.grad_weight_accum,
-           "path": ("flce_forward_backward (one pass, no recompute)" if fused is not None
-                    else "flce_forward + flce_backward (recompute)")}
+           "grad_weight_dtype": wl.grad_weight_dtype or wl.dtype,
+           "vocab_chunk": args.vocab_chunk or "library choice", "vocab_chunks_per_step": plan_chunks,
+           "path": ("flce_forward + flce_backward (the backward recomputes the logit tiles)" if split is not None
+                    else "flce_forward_backward (one pass, no recompute)")}
     out = {
         "metric": METRIC,
-        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": cfg,
-        # the metric's count: 8NHV flop per step (forward logits, recomputed logits, two contractions)
-        "tflops": head["tflops_8nhv"],
-        "frac_of_peak": head["tflops_8nhv"] / peak,
-        "peak_mem_gib": head["peak_mem_gib"],
         "device": _device_info(torch),
         "kernel_source_hash": kernel_source_hash(),
     }
-    if fused is not None:
-        # the one-pass step executes 6NHV (no recompute)
-        out["tflops_executed"] = fused["tflops_executed"]
-        out["frac_of_peak_executed"] = fused["tflops_executed"] / peak
     if split is not None:
-        if fused is not None:
-            out["split_path"] = {"path": "flce_forward + flce_backward (backward recomputes the logit tiles)",
-                                 "ms_per_step": split["ms_per_step"], "value": split["value"],
-                                 "unit": "tokens/s", "tflops": split["tflops_8nhv"],
-                                 "frac_of_peak": split["tflops_8nhv"] / peak, "fwd_ms": split["fwd_ms"],
-                                 "bwd_ms": split["bwd_ms"], "fwd_tflops": split["fwd_tflops"],
-                                 "bwd_tflops": split["bwd_tflops"], "peak_mem_gib": split["peak_mem_gib"]}
-        else:
-            out.update({k: split[k] for k in ("fwd_ms", "bwd_ms", "fwd_tflops", "bwd_tflops")})
-        # the forward tile kernel (flce_forward = the tile kernel plus two finalize kernels of
-        # ~5 us), timed with HIP events on its stream; the one-pass step runs the same kernel
-        # with the logit store on top
-        out["roofline"] = {"bound": "mfma", "kernel": "fwd_tiles_kernel (flce_forward: + finalize)",
-                           "achieved": split["fwd_tflops"], "peak": peak, "unit": "TFLOP/s",
-                           "frac": split["fwd_tflops"] / peak, "traffic": measured_traffic(wl.name)}
+        out.update({
+            "value": split["value"],
+            "ms_per_step": split["ms_per_step"],
+            # the metric's count: 8NHV flop per step (forward logits, recomputed logits, two contractions)
+            "tflops": split["tflops_8nhv"],
+            "frac_of_peak": split["tflops_8nhv"] / peak,
+            "peak_mem_gib": split["peak_mem_gib"],
+            "fwd_ms": split["fwd_ms"], "bwd_ms": split["bwd_ms"],
+            "fwd_tflops": split["fwd_tflops"], "bwd_tflops": split["bwd_tflops"],
+            "kernels": split["kernels"],
+        })
+        # the kernel with the largest share of the step, its launches timed with HIP events on
+        # the stream they run on; achieved = its algorithmic flops per step (2NHV) over its time
+        # per step, i.e. per-launch flops over mean launch duration
+        name, k = max(split["kernels"].items(), key=lambda kv: kv[1]["ms_per_step"])
+        out["roofline"] = {"bound": "mfma", "kernel": name, "achieved": k["tflops"], "peak": peak,
+                           "unit": "TFLOP/s", "frac": k["tflops"] / peak,
+                           "traffic": measured_traffic(name, wl.name),
+                           "launches_per_step": k["launches_per_step"], "mean_launch_ms": k["mean_launch_ms"],
+                           "share_of_step": k["share_of_step"]}
+    else:
+        out.update({"value": fused["value"], "ms_per_step": fused["ms_per_step"],
+                    "tflops_executed": fused["tflops_executed"],
+                    "frac_of_peak_executed": fused["frac_of_peak_executed"], "peak_mem_gib": fused["peak_mem_gib"]})
+    if fused is not None and split is not None:
+        out["one_pass"] = fused
     if not args.no_cpu_baseline:
         del d
         torch.cuda.empty_cache()

@@ -106,6 +106,15 @@ typedef struct {
   float softcap;              /* cap of cap*tanh(v/cap); <= 0 = off                      */
   float z_loss;               /* z-loss multiplier lambda >= 0; 0 = off                  */
   float reserved_f;           /* must be 0                                               */
+  int64_t vocab_chunk;        /* flce_backward: at most this many vocabulary rows per
+                                 chunk of the logit gradient scratch (N x chunk in the
+                                 input dtype; the chunks are balanced over the
+                                 vocabulary), a multiple of 256, or 0 for the
+                                 library's choice; the
+                                 chunk trades scratch size (which decides whether it
+                                 stays in the last-level cache) against one more fp32
+                                 pass over grad_hidden per chunk ("Chunked Linear Loss",
+                                 "Chunk size")                                          */
 } flce_params;
 
 /* Bytes of device workspace one call of `pass` needs (flce_pass).  Host only. */
@@ -194,6 +203,39 @@ int flce_forward_backward(const flce_params* p, int64_t block_rows, const void* 
  */
 int flce_scale_gradients(const flce_params* p, const float* g, void* grad_hidden, void* grad_weight,
                          void* grad_bias, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Launch timing, for benchmarks and profilers: flce_forward_timed and
+ * flce_backward_timed are flce_forward and flce_backward that also record a pair
+ * of caller-owned HIP events on `stream` right before and right after each
+ * launch of a matrix-core kernel, so that one kernel's time can be read inside
+ * a call that launches several.  The events never change what is computed.
+ * ------------------------------------------------------------------------- */
+typedef enum {
+  FLCE_KERNEL_FORWARD_TILES = 1,    /* logit tiles + online softmax (flce_forward)              */
+  FLCE_KERNEL_DLOGITS = 2,          /* recomputed tiles -> logit gradient of a vocabulary chunk */
+  FLCE_KERNEL_GRAD_WEIGHT = 3,      /* grad_weight contraction of a chunk                       */
+  FLCE_KERNEL_GRAD_HIDDEN = 4       /* grad_hidden contraction of a chunk                       */
+} flce_kernel;
+
+typedef struct {
+  void* const* events;   /* 2 * capacity hipEvent_t, created by the caller: pair k is
+                            events[2k] (before the launch) and events[2k+1] (after)   */
+  int32_t* kernel;       /* capacity entries; receives the flce_kernel of each pair    */
+  int32_t capacity;      /* pairs available                                             */
+  int32_t count;         /* in: pairs already used (a call appends after them);
+                            out: pairs used.  Launches past capacity are not timed.   */
+} flce_launch_timer;
+
+/* As flce_forward / flce_backward; `timer` may be NULL (no events).  A failed
+ * event record returns FLCE_ERR_HIP. */
+int flce_forward_timed(const flce_params* p, const void* hidden, const void* weight, const void* bias,
+                       const void* targets, float* loss, float* lse, int64_t* num_correct, float* entropy_sum,
+                       void* workspace, size_t workspace_bytes, void* stream, flce_launch_timer* timer);
+int flce_backward_timed(const flce_params* p, const void* hidden, const void* weight, const void* bias,
+                        const void* targets, const float* lse, const float* grad_loss, void* grad_hidden,
+                        void* grad_weight, void* grad_bias, void* workspace, size_t workspace_bytes, void* stream,
+                        flce_launch_timer* timer);
 
 /*
  * Synchronises `stream`, then reads the status word that the last forward,

@@ -47,7 +47,14 @@ FLCE_GRAD_WEIGHT_ACCUM_IN_OUTPUT = 8
 EXPORTED = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_get_status",
             "flce_status_string", "flce_version", "flce_chunked_workspace_size",
             "flce_chunked_linear_loss", "flce_weighted_mse_chunk", "flce_forward_backward_workspace_size",
-            "flce_forward_backward", "flce_scale_gradients")
+            "flce_forward_backward", "flce_scale_gradients", "flce_forward_timed", "flce_backward_timed")
+
+FLCE_KERNEL_FORWARD_TILES = 1
+FLCE_KERNEL_DLOGITS = 2
+FLCE_KERNEL_GRAD_WEIGHT = 3
+FLCE_KERNEL_GRAD_HIDDEN = 4
+KERNEL_NAMES = {FLCE_KERNEL_FORWARD_TILES: "fwd_tiles_kernel", FLCE_KERNEL_DLOGITS: "bwd_dlogits_kernel",
+                FLCE_KERNEL_GRAD_WEIGHT: "bwd_gw_kernel", FLCE_KERNEL_GRAD_HIDDEN: "bwd_gh_kernel"}
 
 
 class flce_params(ctypes.Structure):
@@ -64,6 +71,16 @@ class flce_params(ctypes.Structure):
         ("softcap", ctypes.c_float),
         ("z_loss", ctypes.c_float),
         ("reserved_f", ctypes.c_float),
+        ("vocab_chunk", ctypes.c_int64),
+    ]
+
+
+class flce_launch_timer(ctypes.Structure):
+    _fields_ = [
+        ("events", ctypes.POINTER(ctypes.c_void_p)),
+        ("kernel", ctypes.POINTER(ctypes.c_int32)),
+        ("capacity", ctypes.c_int32),
+        ("count", ctypes.c_int32),
     ]
 
 
@@ -110,7 +127,9 @@ def load(path: Optional[str] = None):
     global _lib
     if _lib is not None:
         return _lib
-    path = path or LIB_PATH
+    # FLCE_LIB_PATH: another build of the same library (the host-sanitizer build of
+    # linear_cross_entropy_tiled_amd.build --host-sanitizers), for the host-side tests
+    path = path or os.environ.get("FLCE_LIB_PATH") or LIB_PATH
     # torch first: the library links the HIP runtime by soname, and the copy
     # torch ships must be the one in the process (a second runtime loaded
     # ahead of torch's crashes it)
@@ -138,6 +157,11 @@ def load(path: Optional[str] = None):
     lib.flce_forward_backward_workspace_size.restype = ctypes.c_int
     lib.flce_forward_backward.argtypes = [P, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.flce_forward_backward.restype = ctypes.c_int
+    TP = ctypes.POINTER(flce_launch_timer)
+    lib.flce_forward_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, TP]
+    lib.flce_forward_timed.restype = ctypes.c_int
+    lib.flce_backward_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, TP]
+    lib.flce_backward_timed.restype = ctypes.c_int
     lib.flce_scale_gradients.argtypes = [P, vp, vp, vp, vp, vp]
     lib.flce_scale_gradients.restype = ctypes.c_int
     CP = ctypes.POINTER(flce_chunked_params)
@@ -173,6 +197,50 @@ def flce_backward(params, hidden, weight, bias, targets, lse, grad_loss, grad_hi
     return load().flce_backward(ctypes.byref(params), hidden, weight, bias, targets, lse, grad_loss,
                                 grad_hidden, grad_weight, grad_bias, workspace, workspace_bytes,
                                 stream)
+
+
+def flce_forward_timed(params, hidden, weight, bias, targets, loss, lse, num_correct, entropy_sum,
+                       workspace, workspace_bytes, stream, timer) -> int:
+    return load().flce_forward_timed(ctypes.byref(params), hidden, weight, bias, targets, loss, lse,
+                                     num_correct, entropy_sum, workspace, workspace_bytes, stream,
+                                     None if timer is None else ctypes.byref(timer))
+
+
+def flce_backward_timed(params, hidden, weight, bias, targets, lse, grad_loss, grad_hidden, grad_weight,
+                        grad_bias, workspace, workspace_bytes, stream, timer) -> int:
+    return load().flce_backward_timed(ctypes.byref(params), hidden, weight, bias, targets, lse, grad_loss,
+                                      grad_hidden, grad_weight, grad_bias, workspace, workspace_bytes, stream,
+                                      None if timer is None else ctypes.byref(timer))
+
+
+class LaunchTimer:
+    """Host side of flce_launch_timer: `capacity` pairs of caller-owned HIP events (torch
+    events, recorded once on `stream` so that they exist) that flce_forward_timed /
+    flce_backward_timed record around their matrix-core launches.  ``durations()`` maps
+    each kernel name to the milliseconds of its timed launches, after a synchronize."""
+
+    def __init__(self, capacity: int, stream):
+        import torch
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * capacity)]
+        for e in self.events:
+            e.record(stream)
+        handles = [e.cuda_event for e in self.events]
+        if not all(handles):
+            raise RuntimeError("torch did not create the timing events")
+        self._handles = (ctypes.c_void_p * len(handles))(*handles)
+        self._kinds = (ctypes.c_int32 * capacity)()
+        self.c = flce_launch_timer(ctypes.cast(self._handles, ctypes.POINTER(ctypes.c_void_p)),
+                                   ctypes.cast(self._kinds, ctypes.POINTER(ctypes.c_int32)), capacity, 0)
+
+    def reset(self):
+        self.c.count = 0
+
+    def durations(self):
+        out = {}
+        for k in range(self.c.count):
+            ms = self.events[2 * k].elapsed_time(self.events[2 * k + 1])
+            out.setdefault(KERNEL_NAMES.get(self._kinds[k], str(self._kinds[k])), []).append(ms)
+        return out
 
 
 def flce_forward_backward_workspace_size(params: flce_params, block_rows: int = 0) -> int:
@@ -240,7 +308,7 @@ def make_params(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
                 softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
                 reduction: str = "mean", accumulate_grad_weight: bool = False,
                 accumulate_grad_bias: bool = False, targets_int32: bool = False,
-                grad_weight_accum_dtype: str = "fp32") -> flce_params:
+                grad_weight_accum_dtype: str = "fp32", vocab_chunk: int = 0) -> flce_params:
     if reduction not in REDUCTIONS:
         raise ValueError(f"invalid reduction {reduction!r}")
     dt = DTYPES
@@ -252,6 +320,7 @@ def make_params(n_tokens: int, hidden: int, vocab: int, *, dtype: str = "bf16",
     p.logit_scale = logit_scale
     p.softcap = softcap if softcap else 0.0
     p.z_loss = z_loss
+    p.vocab_chunk = vocab_chunk
     p.flags = (FLCE_ACCUMULATE_GRAD_WEIGHT if accumulate_grad_weight else 0) | \
               (FLCE_ACCUMULATE_GRAD_BIAS if accumulate_grad_bias else 0) | \
               (FLCE_TARGETS_INT32 if targets_int32 else 0)
@@ -296,16 +365,76 @@ def _check(t, name):
         raise ValueError(f"{name} must be a contiguous device tensor")
 
 
+def _validate(hidden, weight, targets, bias=None, *, reduction="mean", lse=None, grad_loss=None,
+              grad_weight=None, grad_bias=None):
+    """Host-side checks before anything is launched.  The kernels read weight and bias in
+    hidden's dtype with hidden's row length, targets, lse and the upstream gradient with the
+    lengths N implies, and the gradient buffers with the weight's shape; a mismatch would read
+    or write out of bounds (or silently misread), so it raises TypeError (types) or
+    ValueError (shapes, layout, devices) here instead."""
+    import torch
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"invalid reduction {reduction!r}")
+    if hidden.dim() != 2 or weight.dim() != 2:
+        raise ValueError(f"hidden and weight must be 2-D, got {tuple(hidden.shape)} and {tuple(weight.shape)}")
+    dt = _dtype_name(hidden)
+    n, h = hidden.shape
+    v = weight.shape[0]
+    if weight.dtype != hidden.dtype:
+        raise TypeError(f"weight dtype {weight.dtype} differs from hidden's {hidden.dtype}")
+    if weight.shape[1] != h:
+        raise ValueError(f"weight has {weight.shape[1]} columns, hidden has {h}")
+    if bias is not None:
+        if bias.dtype != hidden.dtype:
+            raise TypeError(f"bias dtype {bias.dtype} differs from hidden's {hidden.dtype}")
+        if bias.dim() != 1 or bias.shape[0] != v:
+            raise ValueError(f"bias must have shape ({v},), got {tuple(bias.shape)}")
+    _targets_int32(targets)
+    if targets.dim() != 1 or targets.shape[0] != n:
+        raise ValueError(f"targets must have shape ({n},), got {tuple(targets.shape)}")
+    if lse is not None:
+        if lse.dtype != torch.float32:
+            raise TypeError(f"lse must be float32, not {lse.dtype}")
+        if lse.numel() != n:
+            raise ValueError(f"lse must hold {n} values, got {lse.numel()}")
+    if grad_loss is not None:
+        if grad_loss.dtype != torch.float32:
+            raise TypeError(f"grad_loss must be float32, not {grad_loss.dtype}")
+        want = n if reduction == "none" else 1
+        if grad_loss.numel() != want and not (reduction == "none" and n == 0):
+            raise ValueError(f"grad_loss must hold {want} value(s) for reduction {reduction!r}, "
+                             f"got {grad_loss.numel()}")
+    if grad_weight is not None:
+        _dtype_name(grad_weight)
+        if tuple(grad_weight.shape) != (v, h):
+            raise ValueError(f"grad_weight must have the weight's shape {(v, h)}, got {tuple(grad_weight.shape)}")
+    if grad_bias is not None:
+        if bias is None:
+            raise ValueError("grad_bias needs a bias")
+        if grad_bias.dtype != bias.dtype:
+            raise TypeError(f"grad_bias dtype {grad_bias.dtype} differs from bias's {bias.dtype}")
+        if tuple(grad_bias.shape) != (v,):
+            raise ValueError(f"grad_bias must have shape ({v},), got {tuple(grad_bias.shape)}")
+    named = [("hidden", hidden), ("weight", weight), ("targets", targets), ("bias", bias), ("lse", lse),
+             ("grad_loss", grad_loss), ("grad_weight", grad_weight), ("grad_bias", grad_bias)]
+    for name, t in named:
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t in named:
+        if t is not None and (t.device.type != "cuda" or t.device != hidden.device):
+            raise ValueError(f"{name} must be on hidden's GPU ({hidden.device}), not {t.device}")
+    return dt
+
+
 def forward(hidden, weight, targets, bias=None, *, logit_scale: float = 1.0,
             softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
             reduction: str = "mean", return_metrics: bool = False, workspace=None):
     """Runs flce_forward on the current stream.  Returns (loss, lse, metrics | None)."""
     import torch
-    for t, n in ((hidden, "hidden"), (weight, "weight"), (targets, "targets"), (bias, "bias")):
-        _check(t, n)
+    dt = _validate(hidden, weight, targets, bias, reduction=reduction)
     n, h = hidden.shape
     v = weight.shape[0]
-    p = make_params(n, h, v, dtype=_dtype_name(hidden), logit_scale=logit_scale, softcap=softcap,
+    p = make_params(n, h, v, dtype=dt, logit_scale=logit_scale, softcap=softcap,
                     z_loss=z_loss, ignore_index=ignore_index, reduction=reduction,
                     targets_int32=_targets_int32(targets))
     dev = hidden.device
@@ -329,28 +458,24 @@ def forward(hidden, weight, targets, bias=None, *, logit_scale: float = 1.0,
 def backward(hidden, weight, targets, lse, grad_loss, bias=None, *, logit_scale: float = 1.0,
              softcap: Optional[float] = None, z_loss: float = 0.0, ignore_index: int = -100,
              reduction: str = "mean", grad_weight_dtype: Optional[str] = None, workspace=None,
-             grad_weight=None, grad_bias=None):
+             grad_weight=None, grad_bias=None, vocab_chunk: int = 0):
     """Runs flce_backward on the current stream.  Returns (grad_hidden, grad_weight, grad_bias).
 
     If ``grad_weight`` (``grad_bias``) is given, the gradient is added to it in place (the
-    FLCE_ACCUMULATE_GRAD_WEIGHT / _BIAS flags) and the same tensor is returned."""
+    FLCE_ACCUMULATE_GRAD_WEIGHT / _BIAS flags) and the same tensor is returned.
+    ``vocab_chunk``: vocabulary rows per chunk of the logit-gradient scratch (a multiple of
+    256; 0 = the library's choice)."""
     import torch
-    for t, n in ((hidden, "hidden"), (weight, "weight"), (targets, "targets"), (bias, "bias"),
-                 (lse, "lse"), (grad_loss, "grad_loss"), (grad_weight, "grad_weight"), (grad_bias, "grad_bias")):
-        _check(t, n)
+    dt = _validate(hidden, weight, targets, bias, reduction=reduction, lse=lse, grad_loss=grad_loss,
+                   grad_weight=grad_weight, grad_bias=grad_bias)
     n, h = hidden.shape
     v = weight.shape[0]
-    dt = _dtype_name(hidden)
     if grad_weight is not None:
         grad_weight_dtype = _dtype_name(grad_weight)
-        if tuple(grad_weight.shape) != (v, h):
-            raise ValueError("grad_weight must have the weight's shape")
-    if grad_bias is not None and (bias is None or grad_bias.dtype != bias.dtype or grad_bias.numel() != v):
-        raise ValueError("grad_bias must match bias")
     p = make_params(n, h, v, dtype=dt, grad_weight_dtype=grad_weight_dtype, logit_scale=logit_scale,
                     softcap=softcap, z_loss=z_loss, ignore_index=ignore_index, reduction=reduction,
                     accumulate_grad_weight=grad_weight is not None, accumulate_grad_bias=grad_bias is not None,
-                    targets_int32=_targets_int32(targets))
+                    targets_int32=_targets_int32(targets), vocab_chunk=vocab_chunk)
     dev = hidden.device
     ws_bytes = flce_workspace_size(p, FLCE_PASS_BACKWARD)
     if workspace is None or workspace.numel() < ws_bytes:
@@ -378,18 +503,12 @@ def forward_backward(hidden, weight, targets, grad_loss, bias=None, *, logit_sca
     ``grad_bias`` given: accumulated into in place, as in ``backward``.  ``grad_weight_accum_dtype``:
     "fp32" (sum over the row blocks in fp32, round once) or "weight" (sum in grad_weight's dtype)."""
     import torch
-    for t, n in ((hidden, "hidden"), (weight, "weight"), (targets, "targets"), (bias, "bias"),
-                 (grad_loss, "grad_loss"), (grad_weight, "grad_weight"), (grad_bias, "grad_bias")):
-        _check(t, n)
+    dt = _validate(hidden, weight, targets, bias, reduction=reduction, grad_loss=grad_loss,
+                   grad_weight=grad_weight, grad_bias=grad_bias)
     n, h = hidden.shape
     v = weight.shape[0]
-    dt = _dtype_name(hidden)
     if grad_weight is not None:
         grad_weight_dtype = _dtype_name(grad_weight)
-        if tuple(grad_weight.shape) != (v, h):
-            raise ValueError("grad_weight must have the weight's shape")
-    if grad_bias is not None and (bias is None or grad_bias.dtype != bias.dtype or grad_bias.numel() != v):
-        raise ValueError("grad_bias must match bias")
     p = make_params(n, h, v, dtype=dt, grad_weight_dtype=grad_weight_dtype, logit_scale=logit_scale,
                     softcap=softcap, z_loss=z_loss, ignore_index=ignore_index, reduction=reduction,
                     accumulate_grad_weight=grad_weight is not None, accumulate_grad_bias=grad_bias is not None,
@@ -500,16 +619,23 @@ def make_chunked_params(n_tokens: int, hidden: int, vocab: int, *, dtype: str = 
 def _run_chunked(inputs, weight, fn, user, *, chunk_rows, grad_weight_dtype, grad_weight_accum_dtype,
                  grad_weight, workspace, on_error=None):
     import torch
-    _check(inputs, "inputs")
-    _check(weight, "weight")
-    _check(grad_weight, "grad_weight")
+    if inputs.dim() != 2 or weight.dim() != 2:
+        raise ValueError(f"inputs and weight must be 2-D, got {tuple(inputs.shape)} and {tuple(weight.shape)}")
     n, h = inputs.shape
     v = weight.shape[0]
     dt = _dtype_name(inputs)
+    if weight.dtype != inputs.dtype:
+        raise TypeError(f"weight dtype {weight.dtype} differs from the inputs' {inputs.dtype}")
+    if weight.shape[1] != h:
+        raise ValueError(f"weight has {weight.shape[1]} columns, inputs have {h}")
     if grad_weight is not None:
         grad_weight_dtype = _dtype_name(grad_weight)
         if tuple(grad_weight.shape) != (v, h):
             raise ValueError("grad_weight must have the weight's shape")
+    for t, nme in ((inputs, "inputs"), (weight, "weight"), (grad_weight, "grad_weight")):
+        _check(t, nme)
+        if t is not None and t.device != inputs.device:
+            raise ValueError(f"{nme} must be on the inputs' GPU")
     p = make_chunked_params(n, h, v, dtype=dt, grad_weight_dtype=grad_weight_dtype,
                             grad_weight_accum_dtype=grad_weight_accum_dtype, chunk_rows=chunk_rows,
                             accumulate_grad_weight=grad_weight is not None)
@@ -591,11 +717,20 @@ def weighted_mse(inputs, weight, target, row_weight, feature_weight, *, chunk_ro
     loss = sum_ij (z_ij - target_ij)^2 row_weight_i feature_weight_j, z = inputs @ weight.T.
     ``target`` is (N, V) fp32 with contiguous rows, the weights fp32 vectors."""
     import torch
+    if weight.dtype != inputs.dtype:
+        raise TypeError(f"weight dtype {weight.dtype} differs from the inputs' {inputs.dtype}")
     for t, nme in ((target, "target"), (row_weight, "row_weight"), (feature_weight, "feature_weight")):
-        if t.dtype != torch.float32 or not t.is_cuda:
-            raise ValueError(f"{nme} must be a float32 device tensor")
+        if t.dtype != torch.float32:
+            raise TypeError(f"{nme} must be float32, not {t.dtype}")
+        if t.device != inputs.device or not t.is_cuda:
+            raise ValueError(f"{nme} must be on the inputs' GPU")
     if target.stride(1) != 1 or not row_weight.is_contiguous() or not feature_weight.is_contiguous():
         raise ValueError("target rows, row_weight and feature_weight must be contiguous")
+    n, v = inputs.shape[0], weight.shape[0]
+    if target.dim() != 2 or target.shape[0] != n or target.shape[1] != v:
+        raise ValueError(f"target must have shape ({n}, {v}), got {tuple(target.shape)}")
+    if row_weight.numel() != n or feature_weight.numel() != v:
+        raise ValueError(f"row_weight must hold {n} values and feature_weight {v}")
     row_loss = torch.empty(inputs.shape[0], dtype=torch.float32, device=inputs.device)
     a = flce_wmse_args(_ptr(target), target.stride(0), _ptr(row_weight), _ptr(feature_weight), _ptr(row_loss))
     return _run_chunked(inputs, weight, weighted_mse_chunk_fn(), ctypes.cast(ctypes.pointer(a), ctypes.c_void_p),

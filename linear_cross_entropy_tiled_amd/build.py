@@ -1,9 +1,17 @@
 """Builds libflce.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-    python -m linear_cross_entropy_tiled_amd.build [--verbose]
+    python -m linear_cross_entropy_tiled_amd.build [--verbose] [--host-sanitizers]
 
 The library is built in-tree, next to this file, so that it travels with the
 source tree.  Every call recompiles.
+
+--host-sanitizers builds libflce_hostsan.so instead: the same sources with the
+host code (argument validation, planning, launch set-up) compiled under
+AddressSanitizer and UndefinedBehaviorSanitizer (-Xarch_host, so the device
+code is built as usual).  It is for host-side tests only: load it with
+FLCE_LIB_PATH pointing at it and the compiler's shared ASan runtime in
+LD_PRELOAD (``sanitizer_runtime()``); tests/test_abi_host_sanitized.py does
+that for the C-ABI validation tests.
 """
 from __future__ import annotations
 
@@ -37,9 +45,35 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libflce.so)")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
+SAN_LIB_PATH = os.path.join(PKG_DIR, "libflce_hostsan.so")
+HOST_SANITIZER_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                        "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def sanitizer_runtime() -> str:
+    """The compiler's shared AddressSanitizer runtime (to preload into a host process)."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE,
+                       stderr=subprocess.DEVNULL)
+    path = r.stdout.decode().strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        import glob
+        hits = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+        if not hits:
+            raise RuntimeError("the shared ASan runtime (libclang_rt.asan-x86_64.so) was not found")
+        path = hits[0]
+    return path
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """libflce_hostsan.so: host code under ASan + UBSan, linked against the shared ASan runtime."""
+    return build(verbose, extra_flags=HOST_SANITIZER_FLAGS, out_path=SAN_LIB_PATH,
+                 link_flags=["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                             "-shared-libasan"], opt="-O1")
+
+
+def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH, link_flags=None, opt: str = "-O3") -> str:
     cc = hipcc()
-    flags = HIPCC_FLAGS + list(extra_flags or [])
+    flags = [f if f != "-O3" else opt for f in HIPCC_FLAGS] + list(extra_flags or [])
     with tempfile.TemporaryDirectory(prefix="flce_build_") as tmp:
         procs = []
         objs = []
@@ -63,17 +97,20 @@ def build(verbose: bool = False, extra_flags=None) -> str:
                 print(text)
         if failed:
             raise RuntimeError(f"hipcc failed for {failed}")
-        tmp_lib = LIB_PATH + ".tmp"
-        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        tmp_lib = out_path + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(link_flags or []), *objs, "-o", tmp_lib]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
         if r.returncode != 0:
             print(r.stdout.decode(errors="replace"), file=sys.stderr)
             raise RuntimeError("linking libflce.so failed")
-        os.replace(tmp_lib, LIB_PATH)
-    return LIB_PATH
+        os.replace(tmp_lib, out_path)
+    return out_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    if "--host-sanitizers" in sys.argv:
+        print(build_host_sanitized(verbose="--verbose" in sys.argv))
+    else:
+        print(build(verbose="--verbose" in sys.argv))

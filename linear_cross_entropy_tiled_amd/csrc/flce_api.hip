@@ -54,6 +54,8 @@ int make_plan(const flce_params* p, Plan* pl) {
     return FLCE_ERR_INVALID_ARG;
   if (!isfinite(p->logit_scale) || !isfinite(p->softcap) || !isfinite(p->z_loss) || p->z_loss < 0.0f)
     return FLCE_ERR_INVALID_ARG;
+  if (p->vocab_chunk < 0) return FLCE_ERR_INVALID_ARG;
+  if (p->vocab_chunk % 256 != 0) return FLCE_ERR_UNSUPPORTED;
   if (p->hidden % 8 != 0) return FLCE_ERR_UNSUPPORTED;
   const int esize = p->dtype == FLCE_F32 ? 4 : 2;
   // 32-bit buffer offsets and int indices inside the kernels
@@ -93,9 +95,12 @@ int make_plan(const flce_params* p, Plan* pl) {
   const int64_t nblk = P.N > 0 ? (P.N + 255) / 256 : 1;
   P.f_bytes = align_up(P.f_blk + size_t(nblk) * sizeof(BlockPart), 256);
 
-  // backward: vocabulary chunks whose dlogits scratch fits the budget
+  // backward: vocabulary chunks of the caller's width, or the widest whose
+  // dlogits scratch fits the budget
   int64_t max_tiles = kMaxChunkTiles;
-  if (P.N_pad > 0) {
+  if (p->vocab_chunk > 0) {
+    max_tiles = p->vocab_chunk / 256;
+  } else if (P.N_pad > 0) {
     const int64_t fit = (int64_t)(kDlogitsBudget / (size_t(P.N_pad) * esize * 256));
     if (fit < max_tiles) max_tiles = fit;
   }
@@ -307,14 +312,18 @@ int flce_workspace_size(const flce_params* p, int pass, size_t* bytes) {
   return FLCE_OK;
 }
 
-int flce_forward(const flce_params* p, const void* hidden, const void* weight, const void* bias,
-                 const void* targets, float* loss, float* lse, int64_t* num_correct,
-                 float* entropy_sum, void* workspace, size_t workspace_bytes, void* stream) {
+static bool timer_ok(const flce_launch_timer* t) {
+  return !t || (t->events && t->kernel && t->capacity >= 0 && t->count >= 0 && t->count <= t->capacity);
+}
+
+int flce_forward_timed(const flce_params* p, const void* hidden, const void* weight, const void* bias,
+                       const void* targets, float* loss, float* lse, int64_t* num_correct, float* entropy_sum,
+                       void* workspace, size_t workspace_bytes, void* stream, flce_launch_timer* timer) {
   Plan pl;
   int rc = make_plan(p, &pl);
   if (rc != FLCE_OK) return rc;
   pl.has_bias = bias != nullptr;
-  if (!workspace) return FLCE_ERR_INVALID_ARG;
+  if (!workspace || !timer_ok(timer)) return FLCE_ERR_INVALID_ARG;
   if (!loss && (pl.reduction != FLCE_REDUCTION_NONE || pl.N > 0)) return FLCE_ERR_INVALID_ARG;
   if (pl.N > 0 && (!hidden || !targets || !lse)) return FLCE_ERR_INVALID_ARG;
   if (!weight) return FLCE_ERR_INVALID_ARG;
@@ -322,20 +331,28 @@ int flce_forward(const flce_params* p, const void* hidden, const void* weight, c
       !aligned16(targets))
     return FLCE_ERR_UNSUPPORTED;
   if (workspace_bytes < pl.f_bytes) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  pl.timer = timer;
   hipError_t e = launch_forward(pl, hidden, weight, bias, targets, loss, lse, num_correct, entropy_sum,
                                 static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
-int flce_backward(const flce_params* p, const void* hidden, const void* weight, const void* bias,
-                  const void* targets, const float* lse, const float* grad_loss, void* grad_hidden,
-                  void* grad_weight, void* grad_bias, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+int flce_forward(const flce_params* p, const void* hidden, const void* weight, const void* bias,
+                 const void* targets, float* loss, float* lse, int64_t* num_correct,
+                 float* entropy_sum, void* workspace, size_t workspace_bytes, void* stream) {
+  return flce_forward_timed(p, hidden, weight, bias, targets, loss, lse, num_correct, entropy_sum, workspace,
+                            workspace_bytes, stream, nullptr);
+}
+
+int flce_backward_timed(const flce_params* p, const void* hidden, const void* weight, const void* bias,
+                        const void* targets, const float* lse, const float* grad_loss, void* grad_hidden,
+                        void* grad_weight, void* grad_bias, void* workspace, size_t workspace_bytes, void* stream,
+                        flce_launch_timer* timer) {
   Plan pl;
   int rc = make_plan(p, &pl);
   if (rc != FLCE_OK) return rc;
   pl.has_bias = bias != nullptr;
-  if (!weight || !grad_weight || !workspace) return FLCE_ERR_INVALID_ARG;
+  if (!weight || !grad_weight || !workspace || !timer_ok(timer)) return FLCE_ERR_INVALID_ARG;
   if (!grad_loss && (pl.reduction != FLCE_REDUCTION_NONE || pl.N > 0)) return FLCE_ERR_INVALID_ARG;
   if (pl.N > 0 && (!hidden || !targets || !lse || !grad_hidden)) return FLCE_ERR_INVALID_ARG;
   if (grad_bias && !bias) return FLCE_ERR_INVALID_ARG;
@@ -343,10 +360,19 @@ int flce_backward(const flce_params* p, const void* hidden, const void* weight, 
       !aligned16(targets) || !aligned16(grad_hidden) || !aligned16(grad_weight) || !aligned16(grad_bias))
     return FLCE_ERR_UNSUPPORTED;
   if (workspace_bytes < pl.b_bytes) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  pl.timer = timer;
   hipError_t e = launch_backward(pl, hidden, weight, bias, targets, lse, grad_loss, grad_hidden,
                                  grad_weight, grad_bias, static_cast<char*>(workspace),
                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+int flce_backward(const flce_params* p, const void* hidden, const void* weight, const void* bias,
+                  const void* targets, const float* lse, const float* grad_loss, void* grad_hidden,
+                  void* grad_weight, void* grad_bias, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return flce_backward_timed(p, hidden, weight, bias, targets, lse, grad_loss, grad_hidden, grad_weight, grad_bias,
+                             workspace, workspace_bytes, stream, nullptr);
 }
 
 int flce_forward_backward_workspace_size(const flce_params* p, int64_t block_rows, size_t* bytes) {

@@ -40,7 +40,7 @@ struct PrepArgs {
   float z_loss;
   float* coefA;   // c_i (1 + 2 lam LSE_i), 0 if ignored
   float* coefB;   // c_i, 0 if ignored
-  float* lseL;    // LSE_i * log2(e)
+  float* lseL;    // LSE_i * log2(e); +inf on padding rows
   int* tgt;       // target or -1
   int* status;
   float* dscale;  // [0] = 2^s, [1] = 2^-s (see above)
@@ -75,7 +75,11 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(PrepArgs a) {
   const float c_all = a.reduction == FLCE_REDUCTION_SUM ? g0 : (n_valid > 0 ? g0 / (float)n_valid : 0.0f);
   float dmax = 0.0f;
   for (int i = a.row0 + tid; i < a.row1; i += 1024) {
-    float ca = 0.0f, cb = 0.0f, ll = 0.0f;
+    // padding rows (i >= N) take LSE = +inf: their logit tiles are the bias
+    // alone, and exp(z - LSE) must be 0 there however large that is (a finite
+    // LSE of 0 overflows exp to inf once |scale * bias| passes ~88, and
+    // inf * coefA = inf * 0 would put NaN into grad_bias and grad_weight)
+    float ca = 0.0f, cb = 0.0f, ll = INFINITY;
     int tg = -1;
     if (i < a.N) {
       const int64_t t = load_target(a.targets, i, a.tgt_i32);
@@ -359,7 +363,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
   }
   if constexpr (sizeof(T) == 2) {
     // the staged logit gradient leaves as whole rows, four 256-byte rows per
-    // store instruction
+    // store instruction (each lane reads rows other lanes wrote)
+    wave_lds_sync();
     const char* src = g_lds + wave * 16384;
     const int q = lane & 15;
     T* dbase = D + (size_t)(t0 + wn * kWaveN + (lane >> 4)) * a.ldD + (vw - a.cv0) + 8 * q;
@@ -442,6 +447,7 @@ __device__ __forceinline__ void block_store_t(float* acc32, OutT* out, int ld,
         *reinterpret_cast<f32x4*>(stage + r_w * 512 + ((ch ^ r_w) << 4)) =
             f32x4{acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]};
       }
+    wave_lds_sync();   // the rows below were written by other lanes
     const int c = lane & 31;
 #pragma unroll
     for (int k0 = 0; k0 < 16; k0 += 4) {
@@ -469,6 +475,7 @@ __device__ __forceinline__ void block_store_t(float* acc32, OutT* out, int ld,
         else store4(out + o, v[0], v[1], v[2], v[3]);
       }
     }
+    wave_lds_sync();   // every lane has read the area before the next tile column is written over it
   }
 }
 
@@ -784,6 +791,7 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       d.ld_gb = (int)pl.V_pad;
       d.dscale = dscale;
       const int nwg = n_vt_c * (int)pl.n_tt;
+      time_begin(pl, st);
       if (pl.has_bias) {
         if (pl.cap > 0) bwd_dlogits_kernel<T, true, true><<<nwg, kThreads, 0, st>>>(d);
         else bwd_dlogits_kernel<T, true, false><<<nwg, kThreads, 0, st>>>(d);
@@ -791,6 +799,7 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
         if (pl.cap > 0) bwd_dlogits_kernel<T, false, true><<<nwg, kThreads, 0, st>>>(d);
         else bwd_dlogits_kernel<T, false, false><<<nwg, kThreads, 0, st>>>(d);
       }
+      time_end(pl, FLCE_KERNEL_DLOGITS, st);
     }
     {
       GwArgs g;
@@ -810,7 +819,9 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       g.accumulate = pl.accum_gw ? 1 : 0;
       g.acc32 = nullptr;
       g.mode = 3;   // each vocabulary row belongs to one chunk: written once
+      time_begin(pl, st);
       launch_gw(pl.dtype, g, st);
+      time_end(pl, FLCE_KERNEL_GRAD_WEIGHT, st);
     }
     if (pl.N > 0) {
       GhArgs h;
@@ -832,7 +843,9 @@ static hipError_t launch_backward_t(const Plan& pl, const void* hidden, const vo
       h.kt_per_part = pl.gh_kt_per_part;
       h.part = reinterpret_cast<float*>(ws + pl.b_ghpart);
       h.dscale = dscale;
+      time_begin(pl, st);
       launch_gh(pl.dtype, h, st);
+      time_end(pl, FLCE_KERNEL_GRAD_HIDDEN, st);
     }
   }
   if (grad_bias) {

@@ -113,7 +113,11 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t nbyt
 // 16-byte direct-to-LDS load: lane l's 16 bytes land at LDS byte address
 // lds_addr + 16 l.  Issued through inline assembly so that the compiler does
 // not treat every later LDS read as dependent on it; the caller waits for
-// vmcnt(0) and synchronises before the data is read.
+// vmcnt(0) and synchronises before the data is read.  The statement sets M0
+// (the LDS address of a direct-to-LDS load) itself.  M0 is a reserved register
+// that a clobber list cannot protect, so correctness rests on the compiler
+// keeping no value of its own in M0 in these kernels; a CPU test compiles the
+// device code and checks that every M0 access is one of these pairs.
 __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
@@ -129,6 +133,17 @@ __device__ __forceinline__ void dma4_sink(const i32x4& rsrc, uint32_t lds_addr, 
                :
                : "s"(lds_addr), "v"(voff), "s"(rsrc)
                : "memory");
+}
+
+// Orders the LDS accesses of one wave whose lanes exchange data through LDS:
+// every access before it, by any lane of the wave, takes effect before any
+// access after it.  A wave's LDS instructions execute in issue order, so this
+// only stops the compiler from moving reads above another lane's writes (or
+// writes above another lane's reads); it emits no wait of its own.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {

@@ -289,8 +289,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
     }
     if constexpr (STORE_Z && sizeof(T) == 2) {
       // the staged logits leave as whole rows, four 256-byte rows per store
-      // instruction; then every wave has read its region back before the next
-      // tile's first stage is loaded over it
+      // instruction (each lane reads rows other lanes wrote); then every wave
+      // has read its region back before the next tile's first stage is loaded
+      // over it
+      wave_lds_sync();
       const char* zst = g_lds + wave * 16384;
       const int q = lane & 15;
       T* zbase = reinterpret_cast<T*>(a.z) + (size_t)(t0 + wn * kWaveN + (lane >> 4)) * a.ldz + vw + 8 * q;
@@ -556,9 +558,11 @@ void launch_forward_rows(const Plan& pl, const void* hidden, const void* weight,
     a.z = z;
     a.ldz = ldz;
     const int nwg = n_tt * S;
+    time_begin(pl, st);
     if (pl.dtype == FLCE_BF16) launch_fwd_tiles<bf16>(pl, a, nwg, st);
     else if (pl.dtype == FLCE_F16) launch_fwd_tiles<f16>(pl, a, nwg, st);
     else launch_fwd_tiles<float>(pl, a, nwg, st);
+    time_end(pl, FLCE_KERNEL_FORWARD_TILES, st);
   }
   const int nblk = n_tt > 0 ? n_tt : 1;
   FinArgs f;

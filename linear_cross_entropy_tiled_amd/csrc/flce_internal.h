@@ -18,6 +18,7 @@ struct Plan {
   bool tgt_i32;                  // targets are int32 (else int64)
   bool gw_accum_out;             // one-pass path: sum grad_weight over the blocks in its own dtype
   float scale, cap, z_loss;
+  flce_launch_timer* timer;      // optional event pairs around the matrix-core launches (caller-owned)
 
   int64_t n_tt, n_vt, n_ht;      // 256-wide tiles over tokens, vocabulary, hidden
   int64_t N_pad, V_pad;          // padded to whole tiles
@@ -49,6 +50,21 @@ struct Plan {
 int forward_splits(int64_t n_tt, int64_t n_vt);
 // Fills the fb_* fields of a plan made by make_plan; block_rows 0 = library choice.
 int plan_forward_backward(Plan* plan, int64_t block_rows);
+
+// flce_launch_timer: one event pair around a launch.  Nothing without a timer
+// or once its capacity is used up; a failed record leaves its error for the
+// hipGetLastError that ends every entry point.
+inline bool timer_open(const Plan& pl) { return pl.timer && pl.timer->count < pl.timer->capacity; }
+inline void time_begin(const Plan& pl, hipStream_t st) {
+  if (timer_open(pl)) (void)hipEventRecord(static_cast<hipEvent_t>(pl.timer->events[2 * pl.timer->count]), st);
+}
+inline void time_end(const Plan& pl, int kernel, hipStream_t st) {
+  if (!timer_open(pl)) return;
+  flce_launch_timer* t = pl.timer;
+  (void)hipEventRecord(static_cast<hipEvent_t>(t->events[2 * t->count + 1]), st);
+  t->kernel[t->count] = kernel;
+  t->count++;
+}
 
 constexpr size_t kStatusBytes = 256;   // status word at workspace offset 0
 // Backward: the dlogits scale factor and its inverse (two fp32 words) follow

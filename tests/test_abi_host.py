@@ -37,9 +37,57 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_struct_layout_matches_header():
-    # 4 x int64, 4 x int32, 4 x float
-    assert ctypes.sizeof(flce.flce_params) == 64
+    # 4 x int64, 4 x int32, 4 x float, int64
+    assert ctypes.sizeof(flce.flce_params) == 72
     assert flce.flce_params.dtype.offset == 32 and flce.flce_params.logit_scale.offset == 48
+    assert flce.flce_params.vocab_chunk.offset == 64
+    # two pointers, two int32
+    assert ctypes.sizeof(flce.flce_launch_timer) == 24 and flce.flce_launch_timer.capacity.offset == 16
+
+
+def test_vocab_chunk_sets_the_scratch(lib):
+    """flce_params.vocab_chunk: the backward's logit-gradient scratch is N_pad x chunk elements;
+    0 is the library's choice; negative or not a multiple of 256 is refused."""
+    n, h, v = 8192, 4096, 128256
+    sizes = {}
+    for vc in (4096, 8192, 16384):
+        p = flce.make_params(n, h, v, dtype="bf16", reduction="sum", softcap=30.0, vocab_chunk=vc)
+        rc, b = _ws(p, flce.FLCE_PASS_BACKWARD)
+        assert rc == 0
+        sizes[vc] = b
+    # chunks of at most vocab_chunk rows, balanced over the 501 vocabulary tiles: widths 4096
+    # (32 chunks), 8192 (16) and 16128 (8); the scratch grows by N * 2 bytes per row of width
+    assert sizes[8192] - sizes[4096] == n * (8192 - 4096) * 2
+    assert sizes[16384] - sizes[8192] == n * (16128 - 8192) * 2
+    for vc, code in ((-256, flce.FLCE_ERR_INVALID_ARG), (1000, flce.FLCE_ERR_UNSUPPORTED)):
+        p = flce.make_params(n, h, v, vocab_chunk=vc)
+        assert _ws(p, flce.FLCE_PASS_BACKWARD)[0] == code
+    # a chunk wider than the vocabulary is one chunk
+    p1 = flce.make_params(512, 64, 1000, vocab_chunk=1 << 20)
+    p0 = flce.make_params(512, 64, 1000)
+    assert _ws(p1, flce.FLCE_PASS_BACKWARD) == _ws(p0, flce.FLCE_PASS_BACKWARD)
+
+
+def test_timed_entry_points_validate_the_timer(lib):
+    p = flce.make_params(64, 64, 100)
+    big = 1 << 30
+    ev = (ctypes.c_void_p * 4)(16, 16, 16, 16)
+    kinds = (ctypes.c_int32 * 2)()
+    E = ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p))
+    K = ctypes.cast(kinds, ctypes.POINTER(ctypes.c_int32))
+    bad = [flce.flce_launch_timer(None, K, 2, 0), flce.flce_launch_timer(E, None, 2, 0),
+           flce.flce_launch_timer(E, K, -1, 0), flce.flce_launch_timer(E, K, 2, 3),
+           flce.flce_launch_timer(E, K, 2, -1)]
+    for t in bad:
+        assert lib.flce_forward_timed(ctypes.byref(p), 16, 16, None, 16, 16, 16, None, None, 16, big, None,
+                                      ctypes.byref(t)) == flce.FLCE_ERR_INVALID_ARG
+        assert lib.flce_backward_timed(ctypes.byref(p), 16, 16, None, 16, 16, 16, 16, 16, None, 16, big, None,
+                                       ctypes.byref(t)) == flce.FLCE_ERR_INVALID_ARG
+    # a valid timer does not hide the other checks
+    ok = flce.flce_launch_timer(E, K, 2, 0)
+    assert lib.flce_forward_timed(ctypes.byref(p), 16, 16, None, 16, 16, 16, None, None, 16, 8, None,
+                                  ctypes.byref(ok)) == flce.FLCE_ERR_WORKSPACE_TOO_SMALL
+    assert ok.count == 0
 
 
 def _ws(p, pass_):
