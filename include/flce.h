@@ -238,6 +238,26 @@ int flce_backward_timed(const flce_params* p, const void* hidden, const void* we
                         flce_launch_timer* timer);
 
 /*
+ * flce_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments as flce_forward without the workspace, same kernels and results.
+ * The scratch flce_forward keeps in its workspace (status word, per-split
+ * softmax partials, per-block sums) lives in a fixed 8 MiB device array inside
+ * the library, one copy per GPU, held until the process ends; the call itself
+ * allocates nothing.  Limit: problems whose forward workspace
+ * (flce_workspace_size, FLCE_PASS_FORWARD) exceeds 8 MiB -- roughly N above
+ * 400k tokens -- return FLCE_ERR_UNSUPPORTED before anything is enqueued.
+ * `stream` must belong to the current device (else FLCE_ERR_INVALID_ARG).
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one GPU
+ * (other streams, other host threads) race and must be serialised by the
+ * caller.  Out-of-range targets are treated as ignored, as in flce_forward, but
+ * there is no workspace whose status word flce_get_status could read.
+ */
+int flce_forward_no_alloc(const flce_params* p, const void* hidden, const void* weight, const void* bias,
+                          const void* targets, float* loss, float* lse, int64_t* num_correct, float* entropy_sum,
+                          void* stream);
+
+/*
  * Synchronises `stream`, then reads the status word that the last forward,
  * backward or forward-backward call on this workspace left: FLCE_OK, FLCE_ERR_TARGET_OUT_OF_RANGE,
  * or FLCE_ERR_HIP if the stream reports an error.

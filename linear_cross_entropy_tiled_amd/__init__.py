@@ -47,7 +47,8 @@ FLCE_GRAD_WEIGHT_ACCUM_IN_OUTPUT = 8
 EXPORTED = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_get_status",
             "flce_status_string", "flce_version", "flce_chunked_workspace_size",
             "flce_chunked_linear_loss", "flce_weighted_mse_chunk", "flce_forward_backward_workspace_size",
-            "flce_forward_backward", "flce_scale_gradients", "flce_forward_timed", "flce_backward_timed")
+            "flce_forward_backward", "flce_scale_gradients", "flce_forward_timed", "flce_backward_timed",
+            "flce_forward_no_alloc")
 
 FLCE_KERNEL_FORWARD_TILES = 1
 FLCE_KERNEL_DLOGITS = 2
@@ -162,6 +163,8 @@ def load(path: Optional[str] = None):
     lib.flce_forward_timed.restype = ctypes.c_int
     lib.flce_backward_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, TP]
     lib.flce_backward_timed.restype = ctypes.c_int
+    lib.flce_forward_no_alloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.flce_forward_no_alloc.restype = ctypes.c_int
     lib.flce_scale_gradients.argtypes = [P, vp, vp, vp, vp, vp]
     lib.flce_scale_gradients.restype = ctypes.c_int
     CP = ctypes.POINTER(flce_chunked_params)
@@ -241,6 +244,12 @@ class LaunchTimer:
             ms = self.events[2 * k].elapsed_time(self.events[2 * k + 1])
             out.setdefault(KERNEL_NAMES.get(self._kinds[k], str(self._kinds[k])), []).append(ms)
         return out
+
+
+def flce_forward_no_alloc(params, hidden, weight, bias, targets, loss, lse, num_correct, entropy_sum,
+                          stream) -> int:
+    return load().flce_forward_no_alloc(ctypes.byref(params), hidden, weight, bias, targets, loss, lse,
+                                        num_correct, entropy_sum, stream)
 
 
 def flce_forward_backward_workspace_size(params: flce_params, block_rows: int = 0) -> int:

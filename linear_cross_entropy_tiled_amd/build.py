@@ -24,7 +24,8 @@ import tempfile
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libflce.so")
-SOURCES = ["flce_api.hip", "flce_forward.hip", "flce_backward.hip", "flce_chunked.hip", "flce_fused.hip"]
+SOURCES = ["flce_api.hip", "flce_forward.hip", "flce_backward.hip", "flce_chunked.hip", "flce_fused.hip",
+           "flce_noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -250,3 +250,17 @@ def test_scale_gradients_validation(lib):
     assert lib.flce_scale_gradients(ctypes.byref(p), 16, 18, 16, None, None) == flce.FLCE_ERR_UNSUPPORTED
     pn = flce.make_params(64, 64, 100, reduction="none")
     assert lib.flce_scale_gradients(ctypes.byref(pn), 16, 16, 16, None, None) == flce.FLCE_ERR_INVALID_ARG
+
+
+def test_forward_no_alloc_refuses_problems_beyond_its_scratch(lib):
+    """flce_forward_no_alloc keeps the forward scratch in a fixed 8 MiB array: a problem whose
+    forward workspace is larger is refused on the host, before any HIP call."""
+    big = flce.make_params(600_000, 64, 1000)
+    assert _ws(big, flce.FLCE_PASS_FORWARD)[1] > 8 << 20
+    assert lib.flce_forward_no_alloc(ctypes.byref(big), 16, 16, None, 16, 16, 16, None, None, None) == \
+        flce.FLCE_ERR_UNSUPPORTED
+    small = flce.make_params(64, 64, 100)
+    assert lib.flce_forward_no_alloc(ctypes.byref(small), 16, None, None, 16, 16, 16, None, None, None) == \
+        flce.FLCE_ERR_INVALID_ARG                     # NULL weight
+    assert lib.flce_forward_no_alloc(ctypes.byref(small), 18, 16, None, 16, 16, 16, None, None, None) == \
+        flce.FLCE_ERR_UNSUPPORTED                     # misaligned hidden
