@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path split|both|fused]
                     [--vocab-chunk C] [--block-rows R] [--grad-weight-accum fp32|weight] [--no-cpu-baseline]
+                    [--power-seconds S]
 
 One step is a full forward + backward (loss, LSE, metrics, grad_hidden,
 grad_weight, grad_bias) on the headline workload: N=8192 tokens, H=4096,
@@ -118,6 +119,57 @@ def cpu_baseline(inp, wl, rows: int):
             "seconds": dt, "gflops": 6.0 * rows * wl.hidden * wl.vocab / dt / 1e9}
 
 
+class PowerSampler:
+    """Read-only board telemetry (socket power, graphics clock) through amdsmi, sampled in a
+    background thread.  The readings refresh about once a second, so it runs over a window of
+    several seconds of steady work, outside the timed steps."""
+
+    def __init__(self, period_s: float = 0.05):
+        import threading
+        import amdsmi
+        self.amdsmi = amdsmi
+        amdsmi.amdsmi_init()
+        self.h = amdsmi.amdsmi_get_processor_handles()[0]
+        self.period = period_s
+        self.samples = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        a = self.amdsmi
+        while not self.stop.is_set():
+            try:
+                p = a.amdsmi_get_power_info(self.h)
+                c = a.amdsmi_get_clock_info(self.h, a.AmdSmiClkType.GFX)
+                self.samples.append((time.perf_counter(), float(p["current_socket_power"]), float(c["clk"])))
+            except Exception:
+                pass
+            self.stop.wait(self.period)
+
+    def __enter__(self):
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.thread.join()
+
+    def summary(self, skip_s: float = 1.5):
+        a = self.amdsmi
+        try:
+            cap = float(a.amdsmi_get_power_cap_info(self.h)["power_cap"]) / 1e6
+        except Exception:
+            cap = None
+        a.amdsmi_shut_down()
+        if not self.samples:
+            return None
+        t0 = self.samples[0][0]
+        s = [(p, c) for t, p, c in self.samples if t - t0 >= skip_s] or [(p, c) for _, p, c in self.samples]
+        return {"socket_power_w_mean": float(np.mean([p for p, _ in s])), "socket_power_w_max": max(p for p, _ in s),
+                "gfx_clock_mhz_mean": float(np.mean([c for _, c in s])), "power_cap_w": cap, "samples": len(s),
+                "note": "amdsmi telemetry over extra untimed steps after the timed ones (first 1.5 s dropped)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +193,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy this many MiB device-to-device once (counter calibration)")
+    ap.add_argument("--power-seconds", type=float, default=0.0,
+                    help="after the timed steps, run steps for this many more seconds while sampling socket power "
+                         "and graphics clock (amdsmi telemetry, read only); reported as `power`")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -256,6 +311,21 @@ def main():
         fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
         bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
         launches = timer.durations()
+        power = None
+        if args.power_seconds > 0:
+            try:
+                sampler = PowerSampler()
+            except Exception as e:   # no telemetry on this machine
+                power = {"error": f"{type(e).__name__}: {e}"}
+            else:
+                with sampler:
+                    t1 = time.perf_counter()
+                    while time.perf_counter() - t1 < args.power_seconds:
+                        for _ in range(4):
+                            fwd(None)
+                            bwd(None)
+                        torch.cuda.synchronize()
+                power = sampler.summary()
         mem = torch.cuda.max_memory_allocated() / 2**30
         del ws_f, ws_b
         torch.cuda.empty_cache()
@@ -271,7 +341,7 @@ def main():
         return {"ms_per_step": step_ms, "value": n / (step_ms * 1e-3), "peak_mem_gib": mem,
                 "tflops_8nhv": flop8 / (step_ms * 1e-3) / 1e12, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
                 "fwd_tflops": 0.25 * flop8 / (fwd_ms * 1e-3) / 1e12,
-                "bwd_tflops": 0.75 * flop8 / (bwd_ms * 1e-3) / 1e12, "kernels": kernels}
+                "bwd_tflops": 0.75 * flop8 / (bwd_ms * 1e-3) / 1e12, "kernels": kernels, "power": power}
 
     split = time_split() if args.path in ("both", "split") else None
     fused = time_fused() if args.path in ("both", "fused") else None
@@ -313,6 +383,8 @@ def main():
             "fwd_tflops": split["fwd_tflops"], "bwd_tflops": split["bwd_tflops"],
             "kernels": split["kernels"],
         })
+        if split["power"] is not None:
+            out["power"] = split["power"]
         # the kernel with the largest share of the step, its launches timed with HIP events on
         # the stream they run on; achieved = its algorithmic flops per step (2NHV) over its time
         # per step, i.e. per-launch flops over mean launch duration
