@@ -25,7 +25,9 @@ def san_env():
         rt = build.sanitizer_runtime()
     except RuntimeError as e:
         pytest.skip(str(e))
-    if not os.path.exists(build.SAN_LIB_PATH):
+    srcs = [os.path.join(build.CSRC, f) for f in os.listdir(build.CSRC)] + [os.path.join(ROOT, "include", "flce.h")]
+    newest = max(os.path.getmtime(f) for f in srcs)
+    if not os.path.exists(build.SAN_LIB_PATH) or os.path.getmtime(build.SAN_LIB_PATH) < newest:
         build.build_host_sanitized()
     env = dict(os.environ)
     env.update(FLCE_LIB_PATH=build.SAN_LIB_PATH, LD_PRELOAD=rt,
