@@ -249,11 +249,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
                  vec_lds + 4096, 256 * E, lane);
   }
 
-  f32x16 acc[kMI][kNI];
+  Acc acc[kMI][kNI];
   zero_acc(acc);
   tile_mainloop<T, true, true>(da, db, KT, grouped_share(vt, tt), acc);
 
-  // ---- epilogue, one 32-row MFMA tile at a time:
+  // ---- epilogue, one 16-row MFMA tile at a time:
   //   D = 2^s * scale * softcap'(z) * (coefA * p - [row = target] * coefB),
   // stored as 4 consecutive vocabulary rows per lane, plus the column sums
   // over this tile's 256 tokens for grad_bias
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
   int rel[kNI];
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
-    const int tl = wn * kWaveN + ni * 32 + (lane & 31);
+    const int tl = wn * kWaveN + acc_col(ni, lane);
     cAs[ni] = reinterpret_cast<const float*>(vec_lds)[tl] * cmul;
     cBs[ni] = reinterpret_cast<const float*>(vec_lds + 1024)[tl] * cmul;
     const float lL = reinterpret_cast<const float*>(vec_lds + 2048)[tl];
@@ -279,28 +279,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
     rel[ni] = reinterpret_cast<const int*>(vec_lds + 3072)[tl] - vw;
   }
   T* D = reinterpret_cast<T*>(a.D);
-  float* xs = reinterpret_cast<float*>(g_stage0);   // [wm][wn][mi][64 lanes]: per-wave column sums
-  float gsum[kMI];
+  float cs[kMI][4];   // per vocabulary row of the lane: the sum over its kNI token columns
 #pragma unroll
   for (int mi = 0; mi < kMI; mi++) {
-    float sb[16];
+    float sb[4];
     if constexpr (HAS_BIAS) {
+      lds_vec4<T>(vec_lds + 4096, wm * kWaveM + acc_row(mi, 0, lane), sb);
 #pragma unroll
-      for (int g = 0; g < 4; g++) {
-        float b4[4];
-        lds_vec4<T>(vec_lds + 4096, wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5), b4);
-#pragma unroll
-        for (int j = 0; j < 4; j++) sb[4 * g + j] = s2 * b4[j];
-      }
+      for (int j = 0; j < 4; j++) sb[j] *= s2;
     }
-    float cs[16];
 #pragma unroll
-    for (int r = 0; r < 16; r++) cs[r] = 0.0f;
+    for (int r = 0; r < 4; r++) cs[mi][r] = 0.0f;
 #pragma unroll
     for (int ni = 0; ni < kNI; ni++) {
-      float f[16], d[16];   // f: softcap' / 4 with the cap, else unused
+      float f[4], d[4];   // f: softcap' / 4 with the cap, else unused
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
+      for (int r = 0; r < 4; r++) {
         const float v = HAS_BIAS ? fmaf(acc[mi][ni][r], s2, sb[r]) : acc[mi][ni][r] * s2;
         if constexpr (SOFTCAP) {
           const float rr = fast_rcp(fast_exp2(v) + 1.0f);
@@ -312,53 +306,35 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
         }
       }
       // the target row, where some lane of the wave holds it here
-      const int rt = rel[ni] - mi * 32;
-      const bool hit = rt >= 0 && rt < 32 && (((rt >> 2) & 1) == (lane >> 5));
+      const int rt = rel[ni] - mi * 16;
+      const bool hit = rt >= 0 && rt < 16 && (rt >> 2) == (lane >> 4);
       if (__builtin_amdgcn_ballot_w64(hit)) {
 #pragma unroll
-        for (int r = 0; r < 16; r++)
+        for (int r = 0; r < 4; r++)
           if (acc_row(0, r, lane) == rt) d[r] -= SOFTCAP ? cBs[ni] * f[r] : cBs[ni];
       }
       if (ragged) {
 #pragma unroll
-        for (int r = 0; r < 16; r++)
+        for (int r = 0; r < 4; r++)
           if (vw + acc_row(mi, r, lane) >= a.V) d[r] = 0.0f;
       }
 #pragma unroll
-      for (int r = 0; r < 16; r++) cs[r] += d[r];
+      for (int r = 0; r < 4; r++) cs[mi][r] += d[r];
       if constexpr (sizeof(T) == 2) {
         // into this wave's 16 KiB of LDS (64 token rows x 128 logits; 16-byte
         // chunk q of row t at chunk q ^ (t & 15)), stored as whole rows below;
-        // the key is opaque so that the offsets are not held across the main loop
-        const int tl = ni * 32 + (lane & 31);
+        // the lane's 4 values are half of chunk 2 mi + lane/32; the key is
+        // opaque so that the offsets are not held across the main loop
+        const int tl = acc_col(ni, lane);
         int key = (tl & 15) << 4;
         asm volatile("" : "+v"(key));
-        char* dst = g_lds + wave * 16384 + tl * 256 + 8 * (lane >> 5);
-#pragma unroll
-        for (int g = 0; g < 4; g++)
-          store4(reinterpret_cast<T*>(dst + (((mi * 4 + g) << 4) ^ key)), d[4 * g], d[4 * g + 1], d[4 * g + 2],
-                 d[4 * g + 3]);
+        char* dst = g_lds + wave * 16384 + tl * 256 + 8 * ((lane >> 4) & 1);
+        const int q = mi * 2 + (lane >> 5);
+        store4(reinterpret_cast<T*>(dst + ((q << 4) ^ key)), d[0], d[1], d[2], d[3]);
       } else {
-        const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
-        T* drow = D + (size_t)t * a.ldD + (vw - a.cv0) + mi * 32 + 4 * (lane >> 5);
-#pragma unroll
-        for (int g = 0; g < 4; g++) store4(drow + 8 * g, d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]);
+        const int t = t0 + wn * kWaveN + acc_col(ni, lane);
+        store4(D + (size_t)t * a.ldD + (vw - a.cv0) + acc_row(mi, 0, lane), d[0], d[1], d[2], d[3]);
       }
-    }
-    if constexpr (HAS_BIAS) {
-      // reduce-scatter the 16 column sums over the 32 lanes of each half;
-      // afterwards lanes 2j and 2j+1 both hold the sum of position r = j
-#pragma unroll
-      for (int n = 8, m = 16; m >= 2; n >>= 1, m >>= 1) {
-        const bool up = (lane & m) != 0;
-#pragma unroll
-        for (int p = 0; p < n; p++) {
-          const float keep = up ? cs[p + n] : cs[p];
-          const float send = up ? cs[p] : cs[p + n];
-          cs[p] = keep + __shfl_xor(send, m);
-        }
-      }
-      gsum[mi] = cs[0] + __shfl_xor(cs[0], 1);
     }
   }
   if constexpr (sizeof(T) == 2) {
@@ -374,24 +350,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
       const i32x4 v = *reinterpret_cast<const i32x4*>(src + r * 256 + ((q ^ (r & 15)) << 4));
       *reinterpret_cast<i32x4*>(dbase + (size_t)(4 * k) * a.ldD) = v;
     }
-    // the column sums below go through LDS over the staging areas
-    if constexpr (HAS_BIAS) __syncthreads();
   }
   if constexpr (HAS_BIAS) {
-    // the kWavesN waves with the same wm hold the same vocabulary rows:
-    // add their column sums in wn order
-#pragma unroll
-    for (int mi = 0; mi < kMI; mi++) xs[((wm * kWavesN + wn) * kMI + mi) * 64 + lane] = gsum[mi];
+    // grad_bias partial of this token tile: every vocabulary row's sum over the
+    // tile's 256 tokens = the 16 lanes x 4 waves (wn) that hold it, added in a
+    // fixed order through LDS, over the staging areas
     __syncthreads();
-    if (wn == 0 && (lane & 1) == 0) {
+    float* xs = reinterpret_cast<float*>(g_stage0);   // [wm][wn][lane/16][lane%16][kMI x 4]
+    f32x4* mine = reinterpret_cast<f32x4*>(xs + ((((wm * kWavesN + wn) * 4 + (lane >> 4)) * 16 + (lane & 15)) * kMI * 4));
 #pragma unroll
-      for (int mi = 0; mi < kMI; mi++) {
-        float sum = xs[((wm * kWavesN + 0) * kMI + mi) * 64 + lane];
+    for (int mi = 0; mi < kMI; mi++) mine[mi] = f32x4{cs[mi][0], cs[mi][1], cs[mi][2], cs[mi][3]};
+    __syncthreads();
+    const int tid2 = threadIdx.x;
+    if (tid2 < 64) {
+      // rows 4 tid2 .. + 3 of the tile: wave row wm, tile mi, lane group g
+      const int wm2 = tid2 >> 5, mi = (tid2 >> 2) & 7, g = tid2 & 3;
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 1; w < kWavesN; w++) sum += xs[((wm * kWavesN + w) * kMI + mi) * 64 + lane];
-        const int row = acc_row(mi, (lane & 31) >> 1, lane);
-        a.gb_part[(size_t)tt * a.ld_gb + vw + row] = sum;
-      }
+      for (int w = 0; w < kWavesN; w++)
+#pragma unroll 4
+        for (int i = 0; i < 16; i++)
+          sum += reinterpret_cast<const f32x4*>(xs + ((((wm2 * kWavesN + w) * 4 + g) * 16 + i) * kMI * 4))[mi];
+      const int row = wm2 * kWaveM + mi * 16 + 4 * g;
+      float* gp = a.gb_part + (size_t)tt * a.ld_gb + v0 + row;
+      *reinterpret_cast<f32x4*>(gp) = sum;
     }
   }
 }
@@ -423,39 +405,36 @@ template <> constexpr bool is_f16<f16>() { return true; }
 // column cbase + c.
 template <typename OutT, int MODE, bool ACC>
 __device__ __forceinline__ void block_store_t(float* acc32, OutT* out, int ld,
-                                              const f32x16 (&acc)[kMI][kNI], float inv, int rbase, int cbase,
+                                              const Acc (&acc)[kMI][kNI], float inv, int rbase, int cbase,
                                               int lane) {
   constexpr bool READ_ACC = MODE == 1 || MODE == 2;
   constexpr bool READ_OUT = ACC && MODE >= 2;
-  // The accumulator holds, per lane, 4 consecutive columns of one row (32 rows
-  // per store instruction, 16 bytes each).  It goes through a 16 KiB LDS
-  // region of this wave's own, one 32-row MFMA tile column at a time, and
+  // The accumulator holds, per lane and tile, 4 consecutive columns of one row
+  // (16 rows per store instruction, 16 bytes each).  It goes through a 16 KiB
+  // LDS region of this wave's own, one 16-row MFMA tile column at a time, and
   // leaves as whole rows: two 128-column rows per instruction, every cache
   // line written whole.  Rows are 512 bytes; the 16-byte chunk c of row r sits
   // at chunk c ^ r, so both the scattered writes and the row reads are free of
   // bank conflicts.  Every LDS read of the main loop whose value is used has
   // completed before it returns, and a wave reads back only what it wrote.
   char* stage = g_lds + (threadIdx.x >> 6) * 16384;
-  const int r_w = lane & 31;
+  const int r_w = lane & 15;
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
 #pragma unroll
-    for (int mi = 0; mi < kMI; mi++)
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int ch = mi * 8 + 2 * g + (lane >> 5);
-        *reinterpret_cast<f32x4*>(stage + r_w * 512 + ((ch ^ r_w) << 4)) =
-            f32x4{acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]};
-      }
+    for (int mi = 0; mi < kMI; mi++) {
+      const int ch = mi * 4 + (lane >> 4);   // columns 4 ch .. 4 ch + 3
+      *reinterpret_cast<f32x4*>(stage + r_w * 512 + ((ch ^ r_w) << 4)) = acc[mi][ni];
+    }
     wave_lds_sync();   // the rows below were written by other lanes
     const int c = lane & 31;
 #pragma unroll
-    for (int k0 = 0; k0 < 16; k0 += 4) {
+    for (int k0 = 0; k0 < 8; k0 += 4) {
       f32x4 pa[4], po[4], cv[4];
 #pragma unroll
       for (int k = 0; k < 4; k++) {
         const int rr = 2 * (k0 + k) + (lane >> 5);
-        const size_t o = (size_t)(rbase + ni * 32 + rr) * ld + cbase + 4 * c;
+        const size_t o = (size_t)(rbase + ni * 16 + rr) * ld + cbase + 4 * c;
         if constexpr (READ_ACC) pa[k] = *reinterpret_cast<const f32x4*>(acc32 + o);
         if constexpr (READ_OUT) po[k] = load4v<OutT>(out + o);
         cv[k] = *reinterpret_cast<const f32x4*>(stage + rr * 512 + ((c ^ rr) << 4));
@@ -463,7 +442,7 @@ __device__ __forceinline__ void block_store_t(float* acc32, OutT* out, int ld,
 #pragma unroll
       for (int k = 0; k < 4; k++) {
         const int rr = 2 * (k0 + k) + (lane >> 5);
-        const size_t o = (size_t)(rbase + ni * 32 + rr) * ld + cbase + 4 * c;
+        const size_t o = (size_t)(rbase + ni * 16 + rr) * ld + cbase + 4 * c;
         float v[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -482,7 +461,7 @@ __device__ __forceinline__ void block_store_t(float* acc32, OutT* out, int ld,
 // Modes 2 and 3 into an output of type OutT.
 template <typename OutT>
 __device__ __forceinline__ void block_store_out(float* acc32, void* out, int ld, int mode, bool accumulate,
-                                                const f32x16 (&acc)[kMI][kNI], float inv, int rbase, int cbase,
+                                                const Acc (&acc)[kMI][kNI], float inv, int rbase, int cbase,
                                                 int lane) {
   OutT* o = reinterpret_cast<OutT*>(out);
   if (mode == 2) {
@@ -496,7 +475,7 @@ __device__ __forceinline__ void block_store_out(float* acc32, void* out, int ld,
 
 // Any mode; out_type is the flce_dtype of `out` (modes 2, 3).
 __device__ __forceinline__ void block_store(float* acc32, void* out, int out_type, int ld, int mode, bool accumulate,
-                                            const f32x16 (&acc)[kMI][kNI], float inv, int rbase, int cbase,
+                                            const Acc (&acc)[kMI][kNI], float inv, int rbase, int cbase,
                                             int lane) {
   if (mode == 0) block_store_t<float, 0, false>(acc32, nullptr, ld, acc, inv, rbase, cbase, lane);
   else if (mode == 1) block_store_t<float, 1, false>(acc32, nullptr, ld, acc, inv, rbase, cbase, lane);
@@ -535,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gw_kernel(GwArgs a) {
   db.k_bytes = 0;
   const int KT = (a.N_pad * E + kBKB - 1) / kBKB;
 
-  f32x16 acc[kMI][kNI];
+  Acc acc[kMI][kNI];
   zero_acc(acc);
   tile_mainloop<T, true, false>(da, db, KT, grouped_share(ht, vt), acc);
 
@@ -547,25 +526,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gw_kernel(GwArgs a) {
   }
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
-    const int v = a.cv0 + vl0 + wn * kWaveN + ni * 32 + (lane & 31);
+    const int v = a.cv0 + vl0 + wn * kWaveN + acc_col(ni, lane);
     if (v >= a.V) continue;
 #pragma unroll
-    for (int mi = 0; mi < kMI; mi++)
+    for (int mi = 0; mi < kMI; mi++) {
+      const int h = h0 + wm * kWaveM + acc_row(mi, 0, lane);   // 4 consecutive h; H % 8 == 0
+      if (h >= a.H) continue;
+      const size_t o = (size_t)v * a.H + h;
+      float c[4] = {acc[mi][ni][0] * inv, acc[mi][ni][1] * inv, acc[mi][ni][2] * inv, acc[mi][ni][3] * inv};
+      if (a.mode == 1 || a.mode == 2) {
+        const f32x4 prev = *reinterpret_cast<const f32x4*>(a.acc32 + o);
 #pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int h = h0 + wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5);
-        if (h >= a.H) continue;
-        const size_t o = (size_t)v * a.H + h;
-        float c[4] = {acc[mi][ni][4 * g] * inv, acc[mi][ni][4 * g + 1] * inv, acc[mi][ni][4 * g + 2] * inv,
-                      acc[mi][ni][4 * g + 3] * inv};
-        if (a.mode == 1 || a.mode == 2) {
-          const f32x4 prev = *reinterpret_cast<const f32x4*>(a.acc32 + o);
-#pragma unroll
-          for (int j = 0; j < 4; j++) c[j] += prev[j];
-        }
-        if (a.mode <= 1) store4(a.acc32 + o, c[0], c[1], c[2], c[3]);
-        else update4(a.gw, o, a.gw_type, a.accumulate != 0, c);
+        for (int j = 0; j < 4; j++) c[j] += prev[j];
       }
+      if (a.mode <= 1) store4(a.acc32 + o, c[0], c[1], c[2], c[3]);
+      else update4(a.gw, o, a.gw_type, a.accumulate != 0, c);
+    }
   }
 }
 
@@ -613,7 +589,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gh_kernel(GhArgs a) {
   db.cols_valid = 0;
   db.k_bytes = (a.cvn - v_off) * E;
 
-  f32x16 acc[kMI][kNI];
+  Acc acc[kMI][kNI];
   zero_acc(acc);
   tile_mainloop<T, false, true>(da, db, KT, grouped_share(ht, tt), acc);
 
@@ -629,35 +605,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gh_kernel(GhArgs a) {
   }
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
-    const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
+    const int t = t0 + wn * kWaveN + acc_col(ni, lane);
     if (t >= a.N) continue;
 #pragma unroll
-    for (int mi = 0; mi < kMI; mi++)
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int h = h0 + wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5);
-        if (h >= a.H) continue;
-        const size_t o = (size_t)t * a.H + h;
-        float c0 = acc[mi][ni][4 * g] * inv, c1 = acc[mi][ni][4 * g + 1] * inv;
-        float c2 = acc[mi][ni][4 * g + 2] * inv, c3 = acc[mi][ni][4 * g + 3] * inv;
-        if (a.parts > 1) {   // partial of this split; bwd_gh_reduce applies the mode
-          store4(a.part + (size_t)split * a.N * a.H + o, c0, c1, c2, c3);
-          continue;
-        }
-        if (a.mode == 1 || a.mode == 2) {
-          const f32x4 prev = *reinterpret_cast<const f32x4*>(a.accb + o);
-          c0 += prev[0];
-          c1 += prev[1];
-          c2 += prev[2];
-          c3 += prev[3];
-        }
-        if (a.mode <= 1 || a.out_f32) {
-          float* dst = (a.mode <= 1) ? a.accb + o : reinterpret_cast<float*>(a.out) + o;
-          store4(dst, c0, c1, c2, c3);
-        } else {
-          store4(reinterpret_cast<T*>(a.out) + o, c0, c1, c2, c3);
-        }
+    for (int mi = 0; mi < kMI; mi++) {
+      const int h = h0 + wm * kWaveM + acc_row(mi, 0, lane);   // 4 consecutive h; H % 8 == 0
+      if (h >= a.H) continue;
+      const size_t o = (size_t)t * a.H + h;
+      float c0 = acc[mi][ni][0] * inv, c1 = acc[mi][ni][1] * inv;
+      float c2 = acc[mi][ni][2] * inv, c3 = acc[mi][ni][3] * inv;
+      if (a.parts > 1) {   // partial of this split; bwd_gh_reduce applies the mode
+        store4(a.part + (size_t)split * a.N * a.H + o, c0, c1, c2, c3);
+        continue;
       }
+      if (a.mode == 1 || a.mode == 2) {
+        const f32x4 prev = *reinterpret_cast<const f32x4*>(a.accb + o);
+        c0 += prev[0];
+        c1 += prev[1];
+        c2 += prev[2];
+        c3 += prev[3];
+      }
+      if (a.mode <= 1 || a.out_f32) {
+        float* dst = (a.mode <= 1) ? a.accb + o : reinterpret_cast<float*>(a.out) + o;
+        store4(dst, c0, c1, c2, c3);
+      } else {
+        store4(reinterpret_cast<T*>(a.out) + o, c0, c1, c2, c3);
+      }
+    }
   }
 }
 

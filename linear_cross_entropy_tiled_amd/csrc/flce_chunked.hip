@@ -67,25 +67,23 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_logits_kernel(LogitsArgs a)
   db.nrec = (uint32_t)max(min(a.rows - t0, 256), 0) * ld;
   db.cols_valid = 0;
   db.k_bytes = a.H * E;
-  f32x16 acc[kMI][kNI];
+  Acc acc[kMI][kNI];
   zero_acc(acc);
   tile_mainloop<T, true, true>(da, db, (a.H * E + kBKB - 1) / kBKB, grouped_share(vt, tt), acc);
 
   T* out = reinterpret_cast<T*>(a.L);
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
-    const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
+    const int t = t0 + wn * kWaveN + acc_col(ni, lane);
     const bool t_ok = t < a.rows;
 #pragma unroll
-    for (int mi = 0; mi < kMI; mi++)
+    for (int mi = 0; mi < kMI; mi++) {
+      const int v = v0 + wm * kWaveM + acc_row(mi, 0, lane);
+      float c[4];
 #pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int v = v0 + wm * kWaveM + acc_row(mi, 4 * g, lane);
-        float c[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) c[j] = (t_ok && v + j < a.V) ? acc[mi][ni][4 * g + j] : 0.0f;
-        store4_t(out + (size_t)t * a.ld + v, c);
-      }
+      for (int j = 0; j < 4; j++) c[j] = (t_ok && v + j < a.V) ? acc[mi][ni][j] : 0.0f;
+      store4_t(out + (size_t)t * a.ld + v, c);
+    }
   }
 }
 

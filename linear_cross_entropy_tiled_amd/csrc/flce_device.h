@@ -4,10 +4,13 @@
 //
 // Tile main loop: C[256 x 256] += A[256 x K] . B[256 x K]^T with fp32
 // accumulation, 8 waves (2 along M x 4 along N, two per SIMD), each wave
-// owning a 128 x 64 block as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16
-// (v_mfma_f32_32x32x16_f16 for fp16, v_mfma_f32_32x32x2_f32 for fp32 inputs).  Two waves per SIMD keep enough
-// LDS reads in flight to feed the matrix cores; with one wave per SIMD
-// (4 x 128 x 128) the same loop measured 6-10% slower.
+// owning a 128 x 64 block as 8 x 4 tiles of v_mfma_f32_16x16x32_bf16
+// (v_mfma_f32_16x16x32_f16 for fp16, v_mfma_f32_16x16x4_f32 for fp32 inputs).
+// The 16x16 tiles move a quarter of the accumulator bytes per instruction of
+// the 32x32 ones, half the register-file bytes per flop with the operands
+// counted: under the board's power cap that is clock, and the same loop with
+// 32x32x16 tiles ran 5-10% slower.  Two waves per SIMD keep enough LDS reads
+// in flight to feed the matrix cores.
 //
 // Both operands are staged through LDS.  Each lives in global memory either
 //   KMAJOR  -- rows are the M (or N) index, K contiguous   (weight and hidden
@@ -16,14 +19,12 @@
 //   MNMAJOR -- rows are the K index, M (or N) contiguous   (the weight and
 //              the dlogits scratch as read by the gradient contractions);
 // MNMAJOR fragments are read with ds_read_b64_tr_b16, which transposes
-// 16-bit elements across each group of 16 lanes.  On gfx950 that read moves
-// about a quarter of the bytes per clock of ds_read_b128, so a contraction
-// uses at most one MNMAJOR operand.
+// 16-bit elements across each group of 16 lanes.
 //
 // K order: a stage is 128 bytes of K per row (64 bf16 or fp16 / 32 fp32), eight
-// 16-byte chunks.  In sub-step s (0..3) lane half h (lane / 32) contracts
-// chunk 4h + s.  Any order is correct as long as both operands use the same
-// one.
+// 16-byte chunks.  In sub-step s (0..1) the lanes of 16-lane group g (lane / 16)
+// contract chunk 4s + g.  Any order is correct as long as both operands use the
+// same one.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,8 +39,6 @@ typedef _Float16 f16;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -58,14 +57,14 @@ constexpr int kBKB = 128;           // bytes of K per pipeline stage per row (64
 constexpr int kWavesM = 2, kWavesN = 4;
 constexpr int kWaves = kWavesM * kWavesN;        // 8 waves
 constexpr int kThreads = 64 * kWaves;            // 512 threads
-constexpr int kMI = 4, kNI = 2;                  // 32 x 32 MFMA tiles per wave (M x N)
-constexpr int kWaveM = 32 * kMI, kWaveN = 32 * kNI;   // 128 x 64
+constexpr int kMI = 8, kNI = 4;                  // 16 x 16 MFMA tiles per wave (M x N)
+constexpr int kWaveM = 16 * kMI, kWaveN = 16 * kNI;   // 128 x 64
 constexpr int kOperandStage = kBM * kBKB;           // one operand's stage: 32 KiB
 constexpr int kStageBytes = 2 * kOperandStage;      // A + B: 64 KiB
 constexpr int kMainLds = 2 * kStageBytes;           // double buffer, 128 KiB
 constexpr int kLoadWaves = kWaves / 2;                          // waves that issue the stage loads
 constexpr int kLoadBlocks = kOperandStage / 1024 / kLoadWaves;  // 1 KiB DMA blocks per loading wave per operand
-constexpr int kSubsteps = 4;
+constexpr int kSubsteps = 2;
 constexpr uint32_t kOob = 0x80000000u;              // buffer offset that reads 0
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -74,11 +73,13 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-// Row (within a 128-row wave block) held by accumulator register r of MFMA
-// tile mi for this lane:  mi*32 + 8*(r/4) + 4*(lane/32) + r%4.
-__device__ __forceinline__ int acc_row(int mi, int r, int lane) {
-  return mi * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
-}
+// Accumulator layout: acc[mi][ni] (4 fp32) holds, for this lane, rows
+// acc_row(mi, r, lane) = mi*16 + 4*(lane/16) + r (r = 0..3, within the wave's
+// 128-row block) of column acc_col(ni, lane) = ni*16 + lane%16 (within its 64).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef f32x4 Acc;
+__device__ __forceinline__ int acc_row(int mi, int r, int lane) { return mi * 16 + ((lane >> 4) << 2) + r; }
+__device__ __forceinline__ int acc_col(int ni, int lane) { return ni * 16 + (lane & 15); }
 
 // ---------------------------------------------------------------------------
 // Operand descriptor and loader.  Loads go straight from global memory
@@ -188,6 +189,7 @@ template <typename T, bool KMAJOR>
 struct OperandLoader {
   i32x4 rsrc;
   uint32_t voff0, voff1;  // lane offsets for even / odd 1 KiB blocks
+  uint32_t voff2, voff3;  // M/N-major 16-bit: the same for blocks with bit 2 of the block index set
   int kc_bytes0, kc_bytes1;   // KMAJOR: the lane's logical chunk column (even / odd blocks)
   int k_bytes;
   uint32_t ld_bytes;
@@ -211,13 +213,19 @@ struct OperandLoader {
       voff0 = (uint32_t)row * d.ld_bytes + kc0 * 16;
       voff1 = (uint32_t)row * d.ld_bytes + kc1 * 16;
     } else if constexpr (sizeof(T) == 2) {
-      // block b holds rows 2b, 2b+1 (512 B each); lane l -> row 2b + l/32, slot l%32
+      // block b holds rows 2b, 2b+1 (512 B each); lane l -> row 2b + l/32,
+      // LDS slot l%32, which holds the row's 16-byte column chunk
+      // slot ^ (4 (row & 3)) ^ (2 ((row >> 3) & 1)); row & 3 follows the parity
+      // of b, and (row >> 3) & 1 = (b >> 2) & 1
       kc_bytes0 = kc_bytes1 = 0;
       const int half = l >> 5, slot = l & 31;
-      const int c_even = slot ^ (4 * (half & 3));          // row & 3 = half      (b even)
-      const int c_odd = slot ^ (4 * ((2 + half) & 3));     // row & 3 = 2 + half  (b odd)
-      voff0 = c_even * 8 < d.cols_valid ? (uint32_t)half * d.ld_bytes + c_even * 16 : kOob;
-      voff1 = c_odd * 8 < d.cols_valid ? (uint32_t)half * d.ld_bytes + c_odd * 16 : kOob;
+      const int c0 = slot ^ (4 * half);                 // b even, (b >> 2) even: row & 3 = half
+      const int c1 = slot ^ (4 * (2 + half));           // b odd: row & 3 = 2 + half
+      const int c2 = c0 ^ 2, c3 = c1 ^ 2;               // the same with (row >> 3) odd
+      voff0 = c0 * 8 < d.cols_valid ? (uint32_t)half * d.ld_bytes + c0 * 16 : kOob;
+      voff1 = c1 * 8 < d.cols_valid ? (uint32_t)half * d.ld_bytes + c1 * 16 : kOob;
+      voff2 = c2 * 8 < d.cols_valid ? (uint32_t)half * d.ld_bytes + c2 * 16 : kOob;
+      voff3 = c3 * 8 < d.cols_valid ? (uint32_t)half * d.ld_bytes + c3 * 16 : kOob;
     } else {
       // fp32: block b is row b (1 KiB); lane l -> chunk l
       kc_bytes0 = kc_bytes1 = 0;
@@ -251,7 +259,8 @@ struct OperandLoader {
                        : ((int)k0 + kc_bytes0 < k_bytes ? voff0 : kOob);
         soff = k0 + (uint32_t)(8 * b) * ld_bytes;
       } else if constexpr (sizeof(T) == 2) {
-        voff = (i & 1) ? voff1 : voff0;
+        static_assert(kLoadBlocks % 8 == 0, "bit 2 of the block index must be that of i");
+        voff = (i & 4) ? ((i & 1) ? voff3 : voff2) : ((i & 1) ? voff1 : voff0);
         soff = ((uint32_t)kt * (kBKB / 2) + 2 * b) * ld_bytes;
       } else {
         voff = voff0;
@@ -268,22 +277,22 @@ __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70
 __device__ __forceinline__ void wait_vmcnt_1() { __builtin_amdgcn_s_waitcnt(0x0F71); }
 
 // ---------------------------------------------------------------------------
-// LDS fragment reads.  `c0` is the first tile row/column of the 32-wide MFMA
-// fragment; lane l gets row/column c0 + l%32 and the 16 bytes of K chunk
-// 4(l/32) + s.
+// LDS fragment reads.  `c0` is the first tile row/column of the 16-wide MFMA
+// fragment; lane l gets row/column c0 + l%16 and the 16 bytes of K chunk
+// 4s + l/16 (sub-step s).
 // ---------------------------------------------------------------------------
 template <typename T, bool KMAJOR> struct Frag;
 
 // KMAJOR rows are 128 B; the 16-byte chunk kc of row r sits at slot
 // kc ^ ((r >> 1) & 7).  A ds_read_b128 is served 16 lanes (16 consecutive
-// rows, two per 256-byte bank line) at a time, and this spreads them over all
-// 64 banks.
+// rows, two per 256-byte bank line, one chunk) at a time, and this spreads them
+// over all 64 banks.
 // (The same reads serve both 16-bit types; only the register type differs.)
 template <typename V8> struct Frag16K {
   typedef V8 type;
   __device__ __forceinline__ static type read(const char* op, int c0, int s, int lane) {
-    const int row = c0 + (lane & 31);
-    const int kc = 4 * (lane >> 5) + s;
+    const int row = c0 + (lane & 15);
+    const int kc = 4 * s + (lane >> 4);
     const int off = row * kBKB + ((kc ^ ((row >> 1) & 7)) << 4);
     return *reinterpret_cast<const V8*>(op + off);
   }
@@ -292,16 +301,21 @@ template <> struct Frag<bf16, true> : Frag16K<bf16x8> {};
 template <> struct Frag<f16, true> : Frag16K<f16x8> {};
 
 // MNMAJOR 16-bit rows are 512 B (256 elements); 8-byte unit u of row r sits at
-// unit u ^ ((r & 3) << 3).  The transposing read gives lane i of each 16-lane
-// group element (4 j' + i/4, i%4) of the 16 chunks its group addressed, so the
-// group addresses rows k..k+3 at columns c, c+4, c+8, c+12.
+// unit u ^ ((r & 3) << 3) ^ (((r >> 3) & 1) << 2).  ds_read_b64_tr_b16 gives
+// lane i of each 16-lane group element i%4 of the 8-byte pieces that lanes
+// i/4, 4 + i/4, 8 + i/4 and 12 + i/4 of the group addressed.  So lane a of
+// group g addresses row 32s + 8g + a/4 (+ 4 for the second read) at columns
+// c0 + 4(a%4) .. + 3, and lane i receives column c0 + i of K rows
+// 32s + 8g .. + 7: its K chunk 4s + g.  The 32 lanes of two groups served
+// together read 4 rows each, one of each row & 3, and the two groups' rows
+// differ in bit 3: all 32 pieces fall in distinct banks.
 template <typename V8> struct Frag16MN {
   typedef V8 type;
   __device__ __forceinline__ static type read(const char* op, int c0, int s, int lane) {
-    const int g = lane >> 4, kk = lane & 15, j = kk >> 2, q = kk & 3;
-    const int row = 32 * (g >> 1) + 8 * s + j;
-    const int u = (c0 >> 2) + 4 * (g & 1) + q;
-    const int off = row * 512 + ((u ^ (j << 3)) << 3);
+    const int g = lane >> 4, a = lane & 15;
+    const int row = 32 * s + 8 * g + (a >> 2);
+    const int u = (c0 >> 2) + (a & 3);
+    const int off = row * 512 + ((u ^ ((row & 3) << 3) ^ ((g & 1) << 2)) << 3);
     i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(op + off));
     i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(op + off + 4 * 512));
     typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -312,22 +326,25 @@ template <typename V8> struct Frag16MN {
 template <> struct Frag<bf16, false> : Frag16MN<bf16x8> {};
 template <> struct Frag<f16, false> : Frag16MN<f16x8> {};
 
-// fp32: chunk kc holds K = 4 kc + j, j = 0..3 (one v_mfma_f32_32x32x2_f32 each).
+// fp32: a stage row is eight 16-byte chunks of 4 floats; lane group g holds
+// chunk 4s + g, and v_mfma_f32_16x16x4_f32 number j of the sub-step contracts
+// element j of every group's chunk (K = 4(4s + g) + j over the four groups).
 template <> struct Frag<float, true> {
   typedef f32x4 type;
   __device__ __forceinline__ static type read(const char* op, int c0, int s, int lane) {
-    const int row = c0 + (lane & 31);
-    const int kc = 4 * (lane >> 5) + s;
+    const int row = c0 + (lane & 15);
+    const int kc = 4 * s + (lane >> 4);
     const int off = row * kBKB + ((kc ^ ((row >> 1) & 7)) << 4);
     return *reinterpret_cast<const f32x4*>(op + off);
   }
 };
 
+// fp32 MNMAJOR rows are 1 KiB (256 floats), unswizzled.
 template <> struct Frag<float, false> {
   typedef f32x4 type;
   __device__ __forceinline__ static type read(const char* op, int c0, int s, int lane) {
-    const int col = c0 + (lane & 31);
-    const int k0 = (4 * (lane >> 5) + s) * 4;
+    const int col = c0 + (lane & 15);
+    const int k0 = (4 * s + (lane >> 4)) * 4;
     f32x4 v;
 #pragma unroll
     for (int j = 0; j < 4; j++) v[j] = *reinterpret_cast<const float*>(op + (k0 + j) * 1024 + col * 4);
@@ -335,15 +352,15 @@ template <> struct Frag<float, false> {
   }
 };
 
-__device__ __forceinline__ void mma(f32x16& c, const bf16x8& a, const bf16x8& b) {
-  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ void mma(Acc& c, const bf16x8& a, const bf16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ void mma(f32x16& c, const f16x8& a, const f16x8& b) {
-  c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ void mma(Acc& c, const f16x8& a, const f16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ void mma(f32x16& c, const f32x4& a, const f32x4& b) {
+__device__ __forceinline__ void mma(Acc& c, const f32x4& a, const f32x4& b) {
 #pragma unroll
-  for (int j = 0; j < 4; j++) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], c, 0, 0, 0);
+  for (int j = 0; j < 4; j++) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -353,37 +370,41 @@ __device__ __forceinline__ void mma(f32x16& c, const f32x4& a, const f32x4& b) {
 static __shared__ __attribute__((aligned(1024))) char g_lds[kMainLds];
 #define g_stage0 (g_lds)
 
-// Fragments of one 16-deep K sub-step: kMI A tiles and kNI B tiles of 32.
+// Fragments in registers: the A fragments of one sub-step (32 deep in K, 16
+// for fp32) plus one spare, and the B fragments of two sub-steps, the current
+// and the next.  Row tile mi < kMI - 1 keeps its A fragment in a[mi], which is
+// overwritten with the next sub-step's as soon as the MFMAs of that row have
+// issued.  The last row tile alternates between a[kMI - 1] (sub-step 0) and
+// the spare a[kMI] (sub-step 1), so that its next fragment is read while the
+// MFMAs still run rather than after them.  In all kMI + 1 + 2 kNI fragments
+// of 4 VGPRs (68) next to the accumulator's 128.
 template <typename T, bool A_KMAJOR, bool B_KMAJOR>
-struct SubstepFrags {
-  typename Frag<T, A_KMAJOR>::type a[kMI];
-  typename Frag<T, B_KMAJOR>::type b[kNI];
+struct MainFrags {
+  typename Frag<T, A_KMAJOR>::type a[kMI + 1];
+  typename Frag<T, B_KMAJOR>::type b[2][kNI];
 
-  __device__ __forceinline__ void read(const char* stage, int s, int wm, int wn, int lane) {
-#pragma unroll
-    for (int i = 0; i < kMI; i++) a[i] = Frag<T, A_KMAJOR>::read(stage, wm * kWaveM + i * 32, s, lane);
+  __device__ __forceinline__ void read_a(const char* stage, int s, int mi, int slot, int wm, int lane) {
+    a[slot] = Frag<T, A_KMAJOR>::read(stage, wm * kWaveM + mi * 16, s, lane);
+  }
+  template <int BUF>
+  __device__ __forceinline__ void read_b(const char* stage, int s, int wn, int lane) {
 #pragma unroll
     for (int i = 0; i < kNI; i++)
-      b[i] = Frag<T, B_KMAJOR>::read(stage + kOperandStage, wn * kWaveN + i * 32, s, lane);
-  }
-  __device__ __forceinline__ void mma_all(f32x16 (&acc)[kMI][kNI]) const {
-#pragma unroll
-    for (int mi = 0; mi < kMI; mi++)
-#pragma unroll
-      for (int ni = 0; ni < kNI; ni++) mma(acc[mi][ni], a[mi], b[ni]);
+      b[BUF][i] = Frag<T, B_KMAJOR>::read(stage + kOperandStage, wn * kWaveN + i * 16, s, lane);
   }
 };
 
 // Shared-tile L2 prefetch.  The 32 workgroups that one XCD runs at once
 // cover a few A tiles and a few B tiles, each read by several of them in step.
 // Workgroup `a_rank` of the `a_n` that read the same A tile fetches its
-// 1/a_n of the tile's lines two stages ahead (likewise for B), so that the
-// others' loads hit in L2 instead of all waiting on the same misses.
+// 1/a_n of the tile's lines kPrefetchAhead stages ahead, one iteration before
+// the stage's loads are issued (likewise for B), so that the others' loads
+// hit in L2 instead of all waiting on the same misses.
 // a_n = 0 (or b_n = 0) turns it off for that operand.
 struct L2Share {
   int a_rank, a_n, b_rank, b_n;
 };
-constexpr int kPrefetchAhead = 2;
+constexpr int kPrefetchAhead = 3;
 static __shared__ __attribute__((aligned(256))) char g_prefetch_sink[256];
 
 // Issues this wave's share of the prefetch of stage kt (16-bit types only); returns
@@ -413,59 +434,55 @@ __device__ __forceinline__ bool prefetch_stage(const OperandLoader<T, A_KMAJOR>&
   }
 }
 
-// Instruction order inside one sub-step (16-bit types): the kMI x kNI = 8 MFMAs with
-// the NR LDS reads of the next sub-step slotted between them, front-loaded so
-// the reads are back before they are needed.  Left to itself the compiler
-// clusters the reads right before their first use and then waits on them.
-template <int NR, int I = 0>
-__device__ __forceinline__ void interleave_mfma_reads() {
-  static_assert(kMI * kNI == 8, "the pattern assumes 8 MFMAs per sub-step");
-  if constexpr (I < 8) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-    constexpr int per = (NR + 5) / 6;
-    constexpr int lo = I * per < NR ? I * per : NR;
-    constexpr int hi = (I + 1) * per < NR ? (I + 1) * per : NR;
-    if constexpr (hi > lo) __builtin_amdgcn_sched_group_barrier(0x100, hi - lo, 0);   // LDS reads
-    interleave_mfma_reads<NR, I + 1>();
-  }
-}
-
-// LDS read instructions per sub-step: one per K-major fragment, two
-// (transposing 8-byte reads) per M/N-major 16-bit fragment.
-template <bool A_KMAJOR, bool B_KMAJOR>
-constexpr int reads_per_substep() {
-  return (A_KMAJOR ? kMI : 2 * kMI) + (B_KMAJOR ? kNI : 2 * kNI);
-}
-
-// One sub-step: MFMAs on `cur` while `nxt` is read from `stage`, sub-step s.
-template <typename T, bool A_KMAJOR, bool B_KMAJOR>
-__device__ __forceinline__ void substep(const SubstepFrags<T, A_KMAJOR, B_KMAJOR>& cur,
-                                        SubstepFrags<T, A_KMAJOR, B_KMAJOR>& nxt, const char* stage, int s,
-                                        int wm, int wn, int lane, f32x16 (&acc)[kMI][kNI]) {
-  if constexpr (sizeof(T) == 2) __builtin_amdgcn_sched_barrier(0);
-  nxt.read(stage, s, wm, wn, lane);
-  cur.mma_all(acc);
-  if constexpr (sizeof(T) == 2) {
-    interleave_mfma_reads<reads_per_substep<A_KMAJOR, B_KMAJOR>()>();
+// One sub-step: the MFMAs of the fragments in registers (B buffer CUR, the
+// last row tile's A in slot kMI - 1 + CUR) while the next sub-step's are read
+// (sub-step s of `stage`): B into the other buffer during row tile 0, A row
+// tile mi - 1 during row tile mi, and the last row tile's into the slot this
+// sub-step does not use, halfway through.  Scheduling barriers fence the row
+// tiles, so that no read is hoisted above the MFMAs whose registers it
+// overwrites (which would need more registers) and none is sunk to right
+// before its first use (where the wave would wait on it).
+template <int CUR, typename T, bool A_KMAJOR, bool B_KMAJOR>
+__device__ __forceinline__ void substep(MainFrags<T, A_KMAJOR, B_KMAJOR>& f, const char* stage, int s, int wm,
+                                        int wn, int lane, Acc (&acc)[kMI][kNI]) {
+  constexpr int kLastCur = kMI - 1 + CUR, kLastNext = kMI - CUR;
+  __builtin_amdgcn_sched_barrier(0);
+  f.template read_b<1 - CUR>(stage, s, wn, lane);
+#pragma unroll
+  for (int ni = 0; ni < kNI; ni++) mma(acc[0][ni], f.a[0], f.b[CUR][ni]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int mi = 1; mi < kMI; mi++) {
+    f.read_a(stage, s, mi - 1, mi - 1, wm, lane);
+    if (mi == kMI / 2) f.read_a(stage, s, kMI - 1, kLastNext, wm, lane);
+    const int slot = mi == kMI - 1 ? kLastCur : mi;
+#pragma unroll
+    for (int ni = 0; ni < kNI; ni++) mma(acc[mi][ni], f.a[slot], f.b[CUR][ni]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // ---------------------------------------------------------------------------
-// The main loop.  Global -> LDS: stage kt+1 streams into one buffer while
-// stage kt is multiplied out of the other.  LDS -> registers: the fragments
-// of sub-step s+1 are read while the 8 MFMAs of sub-step s run, and the
-// first sub-step of the next stage is read right after the stage barrier,
-// under the last MFMAs of the current one.  acc must be zeroed by the
-// caller.  Every LDS read whose value is used completes before the last
-// barrier (the reads after it fill fragments that are discarded), so the
-// caller may write LDS as soon as the loop returns.
+// The main loop.  Global -> LDS: two stage buffers.  Stage kt + 2 is loaded
+// into stage kt's buffer as soon as the barrier in the middle of iteration kt
+// has passed (no wave reads that buffer after it), so each stage's loads have
+// a whole iteration, two sub-steps of MFMAs, to land before the barrier that
+// waits for them.  LDS -> registers: the fragments of sub-step 1 are read
+// while the 32 MFMAs of sub-step 0 run, and those of the first sub-step of the
+// next stage right after the barrier, under the MFMAs of sub-step 1 of the
+// current one.  acc must be zeroed by the caller.  Every LDS read whose value
+// is used completes before the last barrier (the reads after it fill
+// fragments that are discarded), and no load is in flight when the loop
+// returns, so the caller may write LDS at once.
 // ---------------------------------------------------------------------------
 template <typename T, bool A_KMAJOR, bool B_KMAJOR>
 __device__ __forceinline__ void tile_mainloop(const OperandDesc& da, const OperandDesc& db, int KT,
-                                              const L2Share& sh, f32x16 (&acc)[kMI][kNI]) {
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
+                                              const L2Share& sh, Acc (&acc)[kMI][kNI]) {
+  // (opaque, so that a kernel calling this in a loop forms the per-thread
+  // offsets afresh each time instead of keeping them in registers around it)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
 
@@ -481,37 +498,41 @@ __device__ __forceinline__ void tile_mainloop(const OperandDesc& da, const Opera
   wait_loads();
   __syncthreads();
   if (KT <= 0) return;
+  if (KT > 1) {
+    la.load(1, g_lds + kStageBytes);
+    lb.load(1, g_lds + kStageBytes + kOperandStage);
+  }
 
-  SubstepFrags<T, A_KMAJOR, B_KMAJOR> f0, f1;
-  f0.read(g_lds, 0, wm, wn, lane);
+  MainFrags<T, A_KMAJOR, B_KMAJOR> f;
+  f.template read_b<0>(g_lds, 0, wn, lane);
+#pragma unroll
+  for (int mi = 0; mi < kMI; mi++) f.read_a(g_lds, 0, mi, mi, wm, lane);
+  bool pf = false;   // this wave's most recent vector-memory instruction is an L2 prefetch
   for (int kt = 0; kt < KT; ++kt) {
-    const char* cur = g_lds + (kt & 1) * kStageBytes;
-    char* nxt = g_lds + ((kt + 1) & 1) * kStageBytes;
-    if (kt + 1 < KT) {
-      la.load(kt + 1, nxt);
-      lb.load(kt + 1, nxt + kOperandStage);
-    }
-    const bool pf = kt + kPrefetchAhead < KT &&
-                    prefetch_stage<T, A_KMAJOR, B_KMAJOR>(la, lb, sh, kt + kPrefetchAhead, wave, lane);
-    substep(f0, f1, cur, 1, wm, wn, lane, acc);
-    substep(f1, f0, cur, 2, wm, wn, lane, acc);
-    substep(f0, f1, cur, 3, wm, wn, lane, acc);
-    // stage kt+1 must be in LDS; the prefetch issued after it may still be in flight
+    char* cur = g_lds + (kt & 1) * kStageBytes;
+    const char* nxt = g_lds + ((kt + 1) & 1) * kStageBytes;
+    substep<0>(f, cur, 1, wm, wn, lane, acc);
+    // stage kt+1 (loaded during the previous iteration) must be in LDS; a
+    // prefetch issued after it may still be in flight
     if (pf) wait_vmcnt_1();
     else wait_loads();
     __syncthreads();
+    if (kt + 2 < KT) {
+      la.load(kt + 2, cur);
+      lb.load(kt + 2, cur + kOperandStage);
+    }
+    pf = kt + kPrefetchAhead < KT &&
+         prefetch_stage<T, A_KMAJOR, B_KMAJOR>(la, lb, sh, kt + kPrefetchAhead, wave, lane);
     // after the last stage this reads stale (in-bounds) LDS that is never used
-    substep(f1, f0, nxt, 0, wm, wn, lane, acc);
+    substep<1>(f, nxt, 0, wm, wn, lane, acc);
   }
 }
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[kMI][kNI]) {
+__device__ __forceinline__ void zero_acc(Acc (&acc)[kMI][kNI]) {
 #pragma unroll
   for (int mi = 0; mi < kMI; mi++)
 #pragma unroll
-    for (int ni = 0; ni < kNI; ni++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[mi][ni][r] = 0.0f;
+    for (int ni = 0; ni < kNI; ni++) acc[mi][ni] = Acc{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
 // Workgroups are dispatched to the 8 XCDs round-robin (b -> b % 8).  Renumber

@@ -91,18 +91,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int t0 = tt * 256;
 
-  int tgt[kNI];
-  RowState st[kNI];
+  // Running state of the lane's kNI token columns: m and l in registers, the
+  // rest (sum e z, the target logit, the argmax) and the tile's targets in
+  // LDS, where they wait out the main loop without taking its registers.
+  // Every lane reads and writes only its own state slots.
+  static __shared__ float st_T[kWaves][kNI][64], st_zt[kWaves][kNI][64];
+  static __shared__ int st_idx[kWaves][kNI][64], tile_tgt[256];
+  float st_m[kNI], st_l[kNI];
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
-    const int t = t0 + wn * kWaveN + ni * 32 + (lane & 31);
+    st_m[ni] = kMasked;
+    st_l[ni] = 0.0f;
+    st_T[wave][ni][lane] = 0.0f;
+    st_zt[wave][ni][lane] = -INFINITY;
+    st_idx[wave][ni][lane] = 0;
+  }
+  if (tid < 256) {   // visible to all waves after the main loop's first barrier
+    const int t = t0 + tid;
     const int64_t tv = t < a.N ? load_target(a.targets, t, a.tgt_i32) : a.ignore_index;
-    tgt[ni] = (tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1;
-    st[ni].m = kMasked;
-    st[ni].l = 0.0f;
-    st[ni].T = 0.0f;
-    st[ni].zt = -INFINITY;
-    st[ni].idx = 0;
+    tile_tgt[tid] = (tv != a.ignore_index && tv >= 0 && tv < a.V) ? (int)tv : -1;
   }
 
   const uint32_t ld = (uint32_t)a.H * E;
@@ -142,7 +149,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
   const float s_u = SOFTCAP ? a.scale * a.two_log2e_over_cap : a.scale;
   const float k1 = -a.two_cap * kLog2e;
 
-  f32x16 acc[kMI][kNI];
+  Acc acc[kMI][kNI];
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int v0 = vt * 256;
     const char* bias_tile = bias_lds[(vt - vt_begin) & 1];
@@ -161,131 +168,142 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
     zero_acc(acc);
     tile_mainloop<T, true, true>(da, db, KT, sh, acc);
 
-    // ---- epilogue: transform each 32-row MFMA tile and merge it into the
-    // running state of its token column.  Rows are visited in ascending
-    // order, so taking an index only on a strict improvement of the running
-    // max keeps the lowest index on ties.
+    // ---- epilogue: per token column, transform the lane's 32 vocabulary rows of
+    // the tile (4 of each of the 8 row tiles) and merge them into the running
+    // state of the column.  Rows are visited in ascending order, so taking an
+    // index only on a strict improvement of the running max keeps the lowest
+    // index on ties.
     //
     // With the cap, the per-element work is written in u = 2 v log2(e) / cap
     // (v the scaled logit) and r = 1 / (2^u + 1): z = cap (1 - 2r) rises with
     // u, so the block max and argmax are taken on u; e^(z - m) =
     // 2^(r (-2 cap log2e) + (cap - m) log2e); and sum e z = cap sum e -
     // 2 cap sum e r.  Without the cap, u = z.
+    //
+    // Pass 1 overwrites the accumulator with u and takes the lane's max over
+    // the rows below V; pass 2 forms r, the exponentials and the stored
+    // logits.  Nothing but the accumulator holds the column (the registers are
+    // the main loop's).  Rows at or past V (only in the last vocabulary tile)
+    // keep their finite u for the stored logits and are left out of the max,
+    // the argmax and the sums.
+    // Row tests compare the compile-time offset 16 mi + r of an element with a
+    // per-lane bound (acc_row(mi, r, lane) = 16 mi + r + 4 (lane / 16)), so
+    // that no per-element row index is formed and kept in a register.
     const int vw = v0 + wm * kWaveM;
-    const bool ragged = vw + kWaveM > a.V;
+    const int n_valid = a.V - vw;   // rows of the wave block below V
+    const bool ragged = n_valid < kWaveM;
+    const int lane_row = acc_row(0, 0, lane);
+    const int lim = n_valid - lane_row;   // element (mi, r) is below V iff 16 mi + r < lim
 #pragma unroll
-    for (int mi = 0; mi < kMI; mi++) {
-      float sb[16];
-      if constexpr (HAS_BIAS) {
+    for (int ni = 0; ni < kNI; ni++) {
+      float mu = kMasked;
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-          float b4[4];
-          lds_vec4<T>(bias_tile, wm * kWaveM + mi * 32 + 8 * g + 4 * (lane >> 5), b4);
+      for (int mi = 0; mi < kMI; mi++) {
+        float sb[4];
+        if constexpr (HAS_BIAS) {
+          lds_vec4<T>(bias_tile, wm * kWaveM + acc_row(mi, 0, lane), sb);
 #pragma unroll
-          for (int j = 0; j < 4; j++) sb[4 * g + j] = s_u * b4[j];
+          for (int j = 0; j < 4; j++) sb[j] *= s_u;
         }
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+          acc[mi][ni][r] = HAS_BIAS ? fmaf(acc[mi][ni][r], s_u, sb[r]) : acc[mi][ni][r] * s_u;
       }
+      if (ragged) {
 #pragma unroll
-      for (int ni = 0; ni < kNI; ni++) {
-        float u[16], rr[16];
+        for (int mi = 0; mi < kMI; mi++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          u[r] = HAS_BIAS ? fmaf(acc[mi][ni][r], s_u, sb[r]) : acc[mi][ni][r] * s_u;
-          if constexpr (SOFTCAP) rr[r] = fast_rcp(fast_exp2(u[r]) + 1.0f);
+          for (int r = 0; r < 4; r++)
+            if (16 * mi + r < lim) mu = fmaxf(mu, acc[mi][ni][r]);
+      } else {
+#pragma unroll
+        for (int mi = 0; mi < kMI; mi++)
+#pragma unroll
+          for (int r = 0; r < 4; r++) mu = fmaxf(mu, acc[mi][ni][r]);
+      }
+      // the block max in z; a block that is all masked rows keeps kMasked
+      float mx = mu;
+      if constexpr (SOFTCAP) mx = mu == kMasked ? kMasked : fmaf(-a.two_cap, fast_rcp(fast_exp2(mu) + 1.0f), a.cap);
+      // the target logit, where a lane of the wave holds its row here
+      const int rel = tile_tgt[wn * kWaveN + acc_col(ni, lane)] - vw;
+      const bool hit = rel >= 0 && rel < kWaveM && ((rel >> 2) & 3) == (lane >> 4);
+      if (__builtin_amdgcn_ballot_w64(hit)) {
+        const int rel_l = rel - lane_row;
+        float ut = 0.0f;
+#pragma unroll
+        for (int mi = 0; mi < kMI; mi++)
+#pragma unroll
+          for (int r = 0; r < 4; r++)
+            if (16 * mi + r == rel_l) ut = acc[mi][ni][r];
+        if (hit) st_zt[wave][ni][lane] = SOFTCAP ? fmaf(-a.two_cap, fast_rcp(fast_exp2(ut) + 1.0f), a.cap) : ut;
+      }
+      const float m_old = st_m[ni];
+      if (mx > m_old) {   // a new running max: its lowest row in this tile (rows past V come last)
+        int ix = 0;
+#pragma unroll
+        for (int mi = kMI - 1; mi >= 0; mi--)
+#pragma unroll
+          for (int r = 3; r >= 0; r--)
+            if (acc[mi][ni][r] == mu) ix = 16 * mi + r;
+        st_idx[wave][ni][lane] = vw + lane_row + ix;
+      }
+      const float m_new = fmaxf(m_old, mx);
+      const float mL = m_new * kLog2e;
+      const float alpha = fast_exp2(fmaf(m_old, kLog2e, -mL));
+      float se0 = 0.f, se1 = 0.f, sz0 = 0.f, sz1 = 0.f;
+      // with the cap, sz accumulates sum e r
+      const float k0 = fmaf(a.cap, kLog2e, -mL);
+#pragma unroll
+      for (int mi = 0; mi < kMI; mi++) {
+        float z4[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const float u = acc[mi][ni][r];
+          const bool keep = !ragged || 16 * mi + r < lim;
+          float e, w;
+          if constexpr (SOFTCAP) {
+            const float rr = fast_rcp(fast_exp2(u) + 1.0f);
+            z4[r] = fmaf(-a.two_cap, rr, a.cap);
+            w = keep ? rr : 1e30f;   // e = 2^(-huge) = 0, and e r = 0
+            e = fast_exp2(fmaf(w, k1, k0));
+          } else {
+            z4[r] = u;
+            w = keep ? u : kMasked;
+            e = fast_exp2(fmaf(w, kLog2e, -mL));
+          }
+          if (r & 1) {
+            se1 += e;
+            sz1 = fmaf(e, w, sz1);
+          } else {
+            se0 += e;
+            sz0 = fmaf(e, w, sz0);
+          }
         }
         if constexpr (STORE_Z) {
           if constexpr (sizeof(T) == 2) {
             // into this wave's 16 KiB of LDS: 64 token rows x 128 logits (256 B);
-            // 16-byte chunk q of row t sits at chunk q ^ (t & 15)
-            const int tl = ni * 32 + (lane & 31);
+            // 16-byte chunk q of row t sits at chunk q ^ (t & 15); the lane's
+            // 4 logits are half of chunk 2 mi + lane/32
+            const int tl = acc_col(ni, lane);
             // (opaque, so that the swizzled offsets are formed here and not
             // kept in registers across the main loop)
             int key = (tl & 15) << 4;
             asm volatile("" : "+v"(key));
-            char* zst = g_lds + wave * 16384 + tl * 256 + 8 * (lane >> 5);
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-              float z4[4];
-#pragma unroll
-              for (int j = 0; j < 4; j++) z4[j] = SOFTCAP ? fmaf(-a.two_cap, rr[4 * g + j], a.cap) : u[4 * g + j];
-              const int q = mi * 4 + g;   // logits mi*32 + 8g + 4*(lane/32) .. +3
-              store_z4(reinterpret_cast<T*>(zst + ((q << 4) ^ key)), z4);
-            }
+            char* zst = g_lds + wave * 16384 + tl * 256 + 8 * ((lane >> 4) & 1);
+            const int q = mi * 2 + (lane >> 5);
+            store_z4(reinterpret_cast<T*>(zst + ((q << 4) ^ key)), z4);
           } else {
-            const int t = wn * kWaveN + ni * 32 + (lane & 31);   // within this token tile
-            T* zrow = reinterpret_cast<T*>(a.z) + (size_t)(t0 + t) * a.ldz + vw + mi * 32 + 4 * (lane >> 5);
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-              float z4[4];
-#pragma unroll
-              for (int j = 0; j < 4; j++) z4[j] = SOFTCAP ? fmaf(-a.two_cap, rr[4 * g + j], a.cap) : u[4 * g + j];
-              store_z4(zrow + 8 * g, z4);
-            }
+            const int t = wn * kWaveN + acc_col(ni, lane);   // within this token tile
+            T* zrow = reinterpret_cast<T*>(a.z) + (size_t)(t0 + t) * a.ldz + vw + acc_row(mi, 0, lane);
+            store_z4(zrow, z4);
           }
         }
-        if (ragged) {
-#pragma unroll
-          for (int r = 0; r < 16; r++)
-            if (vw + acc_row(mi, r, lane) >= a.V) {
-              u[r] = kMasked;
-              if constexpr (SOFTCAP) rr[r] = 1e30f;   // e = 2^(-huge) = 0, and e r = 0
-            }
-        }
-        float mu = u[0];
-#pragma unroll
-        for (int r = 1; r < 16; r++) mu = fmaxf(mu, u[r]);
-        // the block max in z; a block that is all masked rows keeps kMasked
-        float mx = mu;
-        if constexpr (SOFTCAP) mx = mu == kMasked ? kMasked : fmaf(-a.two_cap, fast_rcp(fast_exp2(mu) + 1.0f), a.cap);
-        // the target logit, where some lane of the wave holds its row here
-        const int rel = tgt[ni] - vw - mi * 32;
-        const bool hit = rel >= 0 && rel < 32 && (((rel >> 2) & 1) == (lane >> 5));
-        if (__builtin_amdgcn_ballot_w64(hit)) {
-#pragma unroll
-          for (int r = 0; r < 16; r++)
-            if (acc_row(0, r, lane) == rel) st[ni].zt = SOFTCAP ? fmaf(-a.two_cap, rr[r], a.cap) : u[r];
-        }
-        const float m_old = st[ni].m;
-        if (mx > m_old) {   // a new running max: its lowest row in this block
-          int ix = 0;
-#pragma unroll
-          for (int r = 15; r >= 0; r--)
-            if (u[r] == mu) ix = acc_row(mi, r, lane);
-          st[ni].idx = vw + ix;
-        }
-        const float m_new = fmaxf(m_old, mx);
-        const float mL = m_new * kLog2e;
-        const float alpha = fast_exp2(fmaf(m_old, kLog2e, -mL));
-        float se0 = 0.f, se1 = 0.f, sz0 = 0.f, sz1 = 0.f;
-        if constexpr (SOFTCAP) {
-          // here sz accumulates sum e r
-          const float k0 = fmaf(a.cap, kLog2e, -mL);
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const float e0 = fast_exp2(fmaf(rr[r], k1, k0));
-            const float e1 = fast_exp2(fmaf(rr[r + 1], k1, k0));
-            se0 += e0;
-            se1 += e1;
-            sz0 = fmaf(e0, rr[r], sz0);
-            sz1 = fmaf(e1, rr[r + 1], sz1);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const float e0 = fast_exp2(fmaf(u[r], kLog2e, -mL));
-            const float e1 = fast_exp2(fmaf(u[r + 1], kLog2e, -mL));
-            se0 += e0;
-            se1 += e1;
-            sz0 = fmaf(e0, u[r], sz0);
-            sz1 = fmaf(e1, u[r + 1], sz1);
-          }
-        }
-        const float se = se0 + se1;
-        const float sz = SOFTCAP ? fmaf(-a.two_cap, sz0 + sz1, a.cap * se) : sz0 + sz1;
-        st[ni].l = fmaf(st[ni].l, alpha, se);
-        st[ni].T = fmaf(st[ni].T, alpha, sz);
-        st[ni].m = m_new;
       }
+      const float se = se0 + se1;
+      const float sz = SOFTCAP ? fmaf(-a.two_cap, sz0 + sz1, a.cap * se) : sz0 + sz1;
+      st_l[ni] = fmaf(st_l[ni], alpha, se);
+      st_T[wave][ni][lane] = fmaf(st_T[wave][ni][lane], alpha, sz);
+      st_m[ni] = m_new;
     }
     if constexpr (STORE_Z && sizeof(T) == 2) {
       // the staged logits leave as whole rows, four 256-byte rows per store
@@ -306,24 +324,37 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
     }
   }
 
-  // ---- merge the two lane halves (same tokens, interleaved rows)
+  RowState st[kNI];
 #pragma unroll
   for (int ni = 0; ni < kNI; ni++) {
-    RowState o;
-    o.m = __shfl_xor(st[ni].m, 32);
-    o.l = __shfl_xor(st[ni].l, 32);
-    o.T = __shfl_xor(st[ni].T, 32);
-    o.zt = __shfl_xor(st[ni].zt, 32);
-    o.idx = __shfl_xor(st[ni].idx, 32);
-    merge_state(st[ni], o);
+    st[ni].m = st_m[ni];
+    st[ni].l = st_l[ni];
+    st[ni].T = st_T[wave][ni][lane];
+    st[ni].zt = st_zt[wave][ni][lane];
+    st[ni].idx = st_idx[wave][ni][lane];
+  }
+  // ---- merge the four lanes of a token column (lanes l, l^16, l^32, l^48: the
+  // same token, rows in disjoint groups of 4)
+#pragma unroll
+  for (int ni = 0; ni < kNI; ni++) {
+#pragma unroll
+    for (int x = 16; x <= 32; x <<= 1) {
+      RowState o;
+      o.m = __shfl_xor(st[ni].m, x);
+      o.l = __shfl_xor(st[ni].l, x);
+      o.T = __shfl_xor(st[ni].T, x);
+      o.zt = __shfl_xor(st[ni].zt, x);
+      o.idx = __shfl_xor(st[ni].idx, x);
+      merge_state(st[ni], o);
+    }
   }
   // ---- merge the two M waves through LDS, then write the split's partials
   static_assert(kWavesM == 2, "the merge below pairs two waves along M");
   float* xs = reinterpret_cast<float*>(g_stage0);   // [wn][field][kWaveN]
-  if (wm == 1 && lane < 32) {
+  if (wm == 1 && lane < 16) {
 #pragma unroll
     for (int ni = 0; ni < kNI; ni++) {
-      const int c = ni * 32 + lane;
+      const int c = acc_col(ni, lane);
       float* p = xs + wn * 5 * kWaveN;
       p[0 * kWaveN + c] = st[ni].m;
       p[1 * kWaveN + c] = st[ni].l;
@@ -333,10 +364,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles_kernel(FwdTileArgs a) {
     }
   }
   __syncthreads();
-  if (wm == 0 && lane < 32) {
+  if (wm == 0 && lane < 16) {
 #pragma unroll
     for (int ni = 0; ni < kNI; ni++) {
-      const int c = ni * 32 + lane;
+      const int c = acc_col(ni, lane);
       const float* p = xs + wn * 5 * kWaveN;
       RowState o;
       o.m = p[0 * kWaveN + c];
