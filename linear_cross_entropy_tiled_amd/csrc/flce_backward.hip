@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
 
   Acc acc[kMI][kNI];
   zero_acc(acc);
-  tile_mainloop<T, true, true>(da, db, KT, grouped_share(vt, tt), acc);
+  tile_mainloop<T, true, true>(da, db, KT, no_share(), acc);
 
   // ---- epilogue, one 16-row MFMA tile at a time:
   //   D = 2^s * scale * softcap'(z) * (coefA * p - [row = target] * coefB),
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gw_kernel(GwArgs a) {
 
   Acc acc[kMI][kNI];
   zero_acc(acc);
-  tile_mainloop<T, true, false>(da, db, KT, grouped_share(ht, vt), acc);
+  tile_mainloop<T, true, false>(da, db, KT, no_share(), acc);
 
   const float inv = a.dscale[1];
   const int vbase = a.cv0 + vl0 + wn * kWaveN, hbase = h0 + wm * kWaveM;

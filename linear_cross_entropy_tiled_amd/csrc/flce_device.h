@@ -197,8 +197,9 @@ struct OperandLoader {
 
   __device__ __forceinline__ void init(const OperandDesc& d, int tid) {
     rsrc = make_rsrc_words(d.base, d.nrec);
-    k_bytes = d.k_bytes;
-    ld_bytes = d.ld_bytes;
+    // (uniform by construction; said so, for descriptors the compiler cannot see through)
+    k_bytes = __builtin_amdgcn_readfirstlane(d.k_bytes);
+    ld_bytes = __builtin_amdgcn_readfirstlane(d.ld_bytes);
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63;
     if constexpr (KMAJOR) {
@@ -552,6 +553,15 @@ __device__ __forceinline__ void grouped_tile(int id, int n_m, int n_n, int gm, i
   const int in = id - group * per_group;
   tm = first + in % size;
   tn = in / size;
+}
+
+// No L2 prefetch (the logit-gradient and grad_weight kernels measured faster
+// without it: their stage loads, issued a full iteration ahead, already find
+// their lines in L2 often enough, and the prefetch costs issue slots).
+__device__ __forceinline__ L2Share no_share() {
+  L2Share s;
+  s.a_rank = s.a_n = s.b_rank = s.b_n = 0;
+  return s;
 }
 
 // Prefetch shares under grouped_tile(..., 4, ...) when one XCD runs 32
