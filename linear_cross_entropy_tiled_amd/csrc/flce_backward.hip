@@ -352,28 +352,43 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
     }
   }
   if constexpr (HAS_BIAS) {
-    // grad_bias partial of this token tile: every vocabulary row's sum over the
-    // tile's 256 tokens = the 16 lanes x 4 waves (wn) that hold it, added in a
-    // fixed order through LDS, over the staging areas
-    __syncthreads();
-    float* xs = reinterpret_cast<float*>(g_stage0);   // [wm][wn][lane/16][lane%16][kMI x 4]
-    f32x4* mine = reinterpret_cast<f32x4*>(xs + ((((wm * kWavesN + wn) * 4 + (lane >> 4)) * 16 + (lane & 15)) * kMI * 4));
+    // grad_bias partial of this token tile: each vocabulary row's sum over the
+    // tile's 256 tokens.  The 16 lanes of a lane group hold the same 32 rows
+    // for 16 tokens each; an exchange that halves the values over lane bits
+    // 3, 2, 1, 0 leaves lane i of group g the sums of its wave's 64 tokens for
+    // values v = 2i, 2i + 1 (v = 4 mi + r: row 16 mi + 4 g + r).  The four
+    // waves along the tokens then add through LDS.  Every step is in a fixed
+    // order, so the sums are reproducible.
+    static __shared__ float gbs[kWaves][kWaveM];
+    float h[4 * kMI];
 #pragma unroll
-    for (int mi = 0; mi < kMI; mi++) mine[mi] = f32x4{cs[mi][0], cs[mi][1], cs[mi][2], cs[mi][3]};
+    for (int mi = 0; mi < kMI; mi++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) h[4 * mi + r] = cs[mi][r];
+#pragma unroll
+    for (int step = 0; step < 4; step++) {
+      const int bit = 8 >> step, half = 16 >> step;
+      const bool hi = (lane & bit) != 0;
+#pragma unroll
+      for (int k = 0; k < half; k++) {
+        const float give = hi ? h[k] : h[half + k];
+        const float keep = hi ? h[half + k] : h[k];
+        h[k] = keep + __shfl_xor(give, bit);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const int v = 2 * (lane & 15) + k;
+      gbs[wave][(v >> 2) * 16 + 4 * (lane >> 4) + (v & 3)] = h[k];
+    }
     __syncthreads();
     const int tid2 = threadIdx.x;
-    if (tid2 < 64) {
-      // rows 4 tid2 .. + 3 of the tile: wave row wm, tile mi, lane group g
-      const int wm2 = tid2 >> 5, mi = (tid2 >> 2) & 7, g = tid2 & 3;
-      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    if (tid2 < 256) {
+      const int wm2 = tid2 / kWaveM, row = tid2 % kWaveM;
+      float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWavesN; w++)
-#pragma unroll 4
-        for (int i = 0; i < 16; i++)
-          sum += reinterpret_cast<const f32x4*>(xs + ((((wm2 * kWavesN + w) * 4 + g) * 16 + i) * kMI * 4))[mi];
-      const int row = wm2 * kWaveM + mi * 16 + 4 * g;
-      float* gp = a.gb_part + (size_t)tt * a.ld_gb + v0 + row;
-      *reinterpret_cast<f32x4*>(gp) = sum;
+      for (int w = 0; w < kWavesN; w++) sum += gbs[wm2 * kWavesN + w][row];
+      a.gb_part[(size_t)tt * a.ld_gb + v0 + tid2] = sum;
     }
   }
 }
