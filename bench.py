@@ -27,6 +27,7 @@ from __future__ import annotations
 import argparse
 import glob
 import hashlib
+import re
 import json
 import os
 import sys
@@ -47,13 +48,21 @@ CSRC = os.path.join(ROOT, "linear_cross_entropy_tiled_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments and with whitespace runs collapsed, so
+    that editing a comment does not count as a change of the kernels."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources; a traffic figure is only reported for the
-    kernels it was measured on."""
+    """Hash of the HIP sources' code (comments and layout ignored); a traffic
+    figure is only reported for the kernels it was measured on."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(CSRC, "*.hip"))):
         h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+        h.update(_code_only(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

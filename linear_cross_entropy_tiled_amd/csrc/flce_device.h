@@ -6,11 +6,11 @@
 // accumulation, 8 waves (2 along M x 4 along N, two per SIMD), each wave
 // owning a 128 x 64 block as 8 x 4 tiles of v_mfma_f32_16x16x32_bf16
 // (v_mfma_f32_16x16x32_f16 for fp16, v_mfma_f32_16x16x4_f32 for fp32 inputs).
-// The 16x16 tiles move a quarter of the accumulator bytes per instruction of
-// the 32x32 ones, half the register-file bytes per flop with the operands
-// counted: under the board's power cap that is clock, and the same loop with
-// 32x32x16 tiles ran 5-10% slower.  Two waves per SIMD keep enough LDS reads
-// in flight to feed the matrix cores.
+// The 16x16 tiles move fewer register-file bytes per flop than 32x32x16 ones
+// (under the board's power cap that is clock); in these kernels they measured
+// within 1% of the 32x32 tiles, a little ahead.  Two waves per SIMD keep
+// enough LDS reads in flight to feed the matrix cores (one wave per SIMD with
+// 128 x 128 wave tiles measured 9% slower).
 //
 // Both operands are staged through LDS.  Each lives in global memory either
 //   KMAJOR  -- rows are the M (or N) index, K contiguous   (weight and hidden
