@@ -457,8 +457,14 @@ __device__ __forceinline__ void substep(MainFrags<T, A_KMAJOR, B_KMAJOR>& f, con
     f.read_a(stage, s, mi - 1, mi - 1, wm, lane);
     if (mi == kMI / 2) f.read_a(stage, s, kMI - 1, kLastNext, wm, lane);
     const int slot = mi == kMI - 1 ? kLastCur : mi;
+    // odd row tiles walk the columns backwards, so that the MFMAs on either side
+    // of a row boundary share their B fragment (fewer operand bits switch: the
+    // step is power-bound, and this measured 1% faster)
 #pragma unroll
-    for (int ni = 0; ni < kNI; ni++) mma(acc[mi][ni], f.a[slot], f.b[CUR][ni]);
+    for (int nj = 0; nj < kNI; nj++) {
+      const int ni = (mi & 1) ? kNI - 1 - nj : nj;
+      mma(acc[mi][ni], f.a[slot], f.b[CUR][ni]);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
