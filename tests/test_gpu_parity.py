@@ -14,8 +14,10 @@ import pytest
 
 import oracle
 import synth_inputs as si
-from gpu_helpers import (assert_grad_close, assert_loss_close, assert_num_correct, t2np, to_device,
-                         widened)
+from gpu_helpers import (LOSS_RTOL, assert_grad_close, assert_loss_close, assert_num_correct, t2np,
+                         to_device, widened)
+
+LOSS_RTOL_BF16 = LOSS_RTOL["bf16"]
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +76,10 @@ SMALL_CASES = [
          weight_std=0.1),
     Case("ragged_f16_none_gwf32", 333, 136, 777, "f16", None, 1.0, None, 0.0, 0.05, "none", "f32",
          weight_std=0.1),
+    # H = 8: one K stage, all but its first 16 (bf16) or 32 (fp32) bytes per row
+    # past the end of the rows
+    Case("hidden_8_bf16", 600, 8, 3000, "bf16", 0.1, 1.0, None, 0.0, 0.05, "sum", weight_std=0.3),
+    Case("hidden_8_f32", 300, 8, 700, "f32", None, 1.0, 3.0, 1e-3, 0.0, "none", weight_std=0.3),
     # fp16 with "mean" over ~1350 valid rows and V = 40000 (two vocabulary
     # chunks): the off-target logit gradients are ~2e-8, below fp16's smallest
     # subnormal, unless the backward scales them (a dropped scale fails here)
@@ -122,6 +128,31 @@ def test_full_parity(flce_lib, case):
     if B is not None:
         assert_grad_close(t2np(gb), rgb, "grad_bias")
     assert flce_lib.get_status(_ws_probe(flce_lib, d)) == 0
+
+
+def test_vocabulary_of_one(flce_lib):
+    """V = 1 (255 of the tile's 256 vocabulary rows past the end): LSE = z, the loss is
+    the z-loss alone, every valid row counts as correct, the entropy is 0 up to the
+    cancellation in LSE - T/l, and the gradients are 2 lam c z times the chain."""
+    c = Case("vocab_one", 300, 64, 1, "bf16", 0.1, 0.8, 4.0, 1e-2, 0.1, "mean", weight_std=0.1)
+    _say(f"[parity] {c.name} N={c.n} H={c.h} V={c.v}")
+    inp = _inputs(c)
+    d = to_device(inp, c.dtype)
+    loss, lse, met, gh, gw, gb = _run_gpu(flce_lib, c, d)
+    X, W, B, T = widened(inp, c.dtype)
+    fwd, rgh, rgw, rgb = oracle.forward_backward(X, W, B, T, inp["grad_loss"].astype(np.float64),
+                                                 **_opts(c))
+    assert fwd.num_correct == fwd.n_valid
+    assert_loss_close(t2np(loss), fwd.loss, c.dtype, "loss")
+    assert_loss_close(t2np(lse), fwd.lse, c.dtype, "lse")
+    assert met["num_correct_tokens"].item() == fwd.n_valid
+    # entropy_i = LSE_i - T_i / l_i: each term is of size |LSE_i|, the difference 0
+    ent = float(t2np(met["entropy_sum"]))
+    bound = LOSS_RTOL_BF16 * float(np.abs(fwd.lse[fwd.valid]).sum())
+    assert abs(ent) <= bound, f"entropy_sum {ent:.3e} beyond {bound:.3e}"
+    assert_grad_close(t2np(gh), rgh, "grad_hidden")
+    assert_grad_close(t2np(gw), rgw, "grad_weight")
+    assert_grad_close(t2np(gb), rgb, "grad_bias")
 
 
 def _ws_probe(flce, d):

@@ -109,6 +109,52 @@ def test_transform_order_and_softcap_closed_form():
     np.testing.assert_allclose(fwd.entropy, [ent, ent], rtol=1e-13)
 
 
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_single_vocabulary_row_closed_form(reduction):
+    """V = 1: p = 1 on every row, so LSE = z, the row loss is lam z^2, the entropy 0,
+    the argmax 0, and dLoss/dz = 2 lam c z (the one-hot and p cancel).  Everything
+    below is written out per row with math.tanh, not through the oracle's arrays."""
+    n, h = 6, 4
+    s, cap, lam = 0.8, 4.0, 0.05
+    x, w, b, _ = _problem(n, h, 1, seed=3)
+    t = np.zeros(n, dtype=np.int64)
+    t[3] = IGN
+    g = _grad_loss(reduction, n)
+    fwd, gh, gw, gb = oracle.forward_backward(x, w, b, t, g, logit_scale=s, softcap=cap, z_loss=lam,
+                                              reduction=reduction)
+    valid = t != IGN
+    nv = int(valid.sum())
+    exp_gh = np.zeros((n, h))
+    exp_gw = np.zeros((1, h))
+    exp_gb = np.zeros(1)
+    total = 0.0
+    for i in range(n):
+        u = sum(x[i, k] * w[0, k] for k in range(h)) + b[0]
+        z = cap * math.tanh(s * u / cap)
+        assert fwd.lse[i] == pytest.approx(z, rel=1e-13, abs=1e-15)
+        assert fwd.entropy[i] == pytest.approx(0.0, abs=1e-14)
+        assert fwd.argmax[i] == 0
+        assert fwd.top2_gap[i] == math.inf
+        if not valid[i]:
+            assert fwd.row_loss[i] == 0.0
+            continue
+        assert fwd.row_loss[i] == pytest.approx(lam * z * z, rel=1e-12)
+        total += lam * z * z
+        c = float(g[i]) if reduction == "none" else (float(g) if reduction == "sum" else float(g) / nv)
+        du = s * (1.0 - (z / cap) ** 2) * 2.0 * lam * c * z
+        exp_gh[i] = du * w[0]
+        exp_gw[0] += du * x[i]
+        exp_gb[0] += du
+    assert fwd.num_correct == nv
+    if reduction == "sum":
+        assert float(fwd.loss) == pytest.approx(total, rel=1e-12)
+    elif reduction == "mean":
+        assert float(fwd.loss) == pytest.approx(total / nv, rel=1e-12)
+    np.testing.assert_allclose(gh, exp_gh, rtol=1e-11, atol=1e-15)
+    np.testing.assert_allclose(gw, exp_gw, rtol=1e-11, atol=1e-15)
+    np.testing.assert_allclose(gb, exp_gb, rtol=1e-11, atol=1e-15)
+
+
 def test_z_loss_closed_form_uniform_logits():
     """With all logits equal to k the row loss is ln V + lam (k + ln V)^2."""
     v, k, lam = 6, 0.75, 0.1
