@@ -207,6 +207,29 @@ struct DlogitsArgs {
   const float* dscale;   // [0]: factor D is stored with
 };
 
+// DPP lane permutations within each 16-lane row, each an involution that
+// pairs lanes differing in one bit of the lane index (and keeps the bits
+// above it): row mirror (i <-> 15 - i: bit 3), half-row mirror (i <-> 7 - i
+// within 8: bit 2), and the quad permutations [2 3 0 1] (bit 1) and
+// [1 0 3 2] (bit 0).
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141, kDppQuadXor2 = 0x4E, kDppQuadXor1 = 0xB1;
+
+// One halving step of an exchange reduction over the 16 lanes of a row: the
+// lane and its partner (CTRL, which flips lane bit BIT) each keep one half of
+// the 2 HALF values, the lane with bit BIT set the upper half, and add the
+// partner's copy of that half.
+template <int HALF, int BIT, int CTRL>
+__device__ __forceinline__ void halve_exchange(float (&h)[32], int lane) {
+  const bool hi = (lane & BIT) != 0;
+#pragma unroll
+  for (int k = 0; k < HALF; k++) {
+    const float give = hi ? h[k] : h[HALF + k];
+    const float keep = hi ? h[HALF + k] : h[k];
+    const int got = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, give), CTRL, 0xF, 0xF, false);
+    h[k] = keep + __builtin_bit_cast(float, got);
+  }
+}
+
 template <typename T, bool HAS_BIAS, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a) {
   constexpr int E = sizeof(T);
@@ -278,6 +301,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
     k0[ni] = SOFTCAP ? fmaf(a.cap, kLog2e, -lL) : -lL;
     rel[ni] = reinterpret_cast<const int*>(vec_lds + 3072)[tl] - vw;
   }
+  // whether any lane's target row lies in this wave's 128 rows, per column tile
+  // (uniform; at large V almost never, so the per-row-tile test below is skipped)
+  bool col_hit[kNI];
+#pragma unroll
+  for (int ni = 0; ni < kNI; ni++) col_hit[ni] = __builtin_amdgcn_ballot_w64(rel[ni] >= 0 && rel[ni] < kWaveM) != 0;
   T* D = reinterpret_cast<T*>(a.D);
   float cs[kMI][4];   // per vocabulary row of the lane: the sum over its kNI token columns
 #pragma unroll
@@ -306,12 +334,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
         }
       }
       // the target row, where some lane of the wave holds it here
-      const int rt = rel[ni] - mi * 16;
-      const bool hit = rt >= 0 && rt < 16 && (rt >> 2) == (lane >> 4);
-      if (__builtin_amdgcn_ballot_w64(hit)) {
+      if (col_hit[ni]) {
+        const int rt = rel[ni] - mi * 16;
+        const bool hit = rt >= 0 && rt < 16 && (rt >> 2) == (lane >> 4);
+        if (__builtin_amdgcn_ballot_w64(hit)) {
 #pragma unroll
-        for (int r = 0; r < 4; r++)
-          if (acc_row(0, r, lane) == rt) d[r] -= SOFTCAP ? cBs[ni] * f[r] : cBs[ni];
+          for (int r = 0; r < 4; r++)
+            if (acc_row(0, r, lane) == rt) d[r] -= SOFTCAP ? cBs[ni] * f[r] : cBs[ni];
+        }
       }
       if (ragged) {
 #pragma unroll
@@ -355,27 +385,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
     // grad_bias partial of this token tile: each vocabulary row's sum over the
     // tile's 256 tokens.  The 16 lanes of a lane group hold the same 32 rows
     // for 16 tokens each; an exchange that halves the values over lane bits
-    // 3, 2, 1, 0 leaves lane i of group g the sums of its wave's 64 tokens for
-    // values v = 2i, 2i + 1 (v = 4 mi + r: row 16 mi + 4 g + r).  The four
-    // waves along the tokens then add through LDS.  Every step is in a fixed
-    // order, so the sums are reproducible.
+    // 3, 2, 1, 0 (partners from DPP permutations within the 16-lane row)
+    // leaves lane i of group g the sums of its wave's 64 tokens for values
+    // v = 2i, 2i + 1 (v = 4 mi + r: row 16 mi + 4 g + r).  The four waves
+    // along the tokens then add through LDS.  Every step is in a fixed order,
+    // so the sums are reproducible.
     static __shared__ float gbs[kWaves][kWaveM];
     float h[4 * kMI];
 #pragma unroll
     for (int mi = 0; mi < kMI; mi++)
 #pragma unroll
       for (int r = 0; r < 4; r++) h[4 * mi + r] = cs[mi][r];
-#pragma unroll
-    for (int step = 0; step < 4; step++) {
-      const int bit = 8 >> step, half = 16 >> step;
-      const bool hi = (lane & bit) != 0;
-#pragma unroll
-      for (int k = 0; k < half; k++) {
-        const float give = hi ? h[k] : h[half + k];
-        const float keep = hi ? h[half + k] : h[k];
-        h[k] = keep + __shfl_xor(give, bit);
-      }
-    }
+    halve_exchange<16, 8, kDppRowMirror>(h, lane);
+    halve_exchange<8, 4, kDppRowHalfMirror>(h, lane);
+    halve_exchange<4, 2, kDppQuadXor2>(h, lane);
+    halve_exchange<2, 1, kDppQuadXor1>(h, lane);
 #pragma unroll
     for (int k = 0; k < 2; k++) {
       const int v = 2 * (lane & 15) + k;
