@@ -369,7 +369,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
   }
   if constexpr (sizeof(T) == 2) {
     // the staged logit gradient leaves as whole rows, four 256-byte rows per
-    // store instruction (each lane reads rows other lanes wrote)
+    // store instruction (each lane reads rows other lanes wrote); non-temporal,
+    // since only later launches read it back (a chunk is far larger than L2),
+    // so that it does not displace operand lines other workgroups still read
     wave_lds_sync();
     const char* src = g_lds + wave * 16384;
     const int q = lane & 15;
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dlogits_kernel(DlogitsArgs a)
     for (int k = 0; k < 16; k++) {
       const int r = 4 * k + (lane >> 4);
       const i32x4 v = *reinterpret_cast<const i32x4*>(src + r * 256 + ((q ^ (r & 15)) << 4));
-      *reinterpret_cast<i32x4*>(dbase + (size_t)(4 * k) * a.ldD) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(dbase + (size_t)(4 * k) * a.ldD));
     }
   }
   if constexpr (HAS_BIAS) {
