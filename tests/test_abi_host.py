@@ -165,6 +165,18 @@ def test_too_large_problem_rejected(lib):
     assert _ws(p, flce.FLCE_PASS_FORWARD)[0] == flce.FLCE_ERR_UNSUPPORTED
 
 
+def test_hidden_size_limit_is_exact(lib):
+    # N*H*esize must stay below 2^31 bytes: 262136 x 4096 bf16 is the largest multiple
+    # of 8 rows that fits (2^31 - 64 KiB), 262144 rows is exactly 2^31
+    for n, ok in ((262136, True), (262144, False)):
+        p = flce.make_params(n, 4096, 64)
+        for pass_ in (flce.FLCE_PASS_FORWARD, flce.FLCE_PASS_BACKWARD):
+            rc = _ws(p, pass_)[0]
+            assert (rc == flce.FLCE_OK) == ok, (n, pass_, rc)
+            if not ok:
+                assert rc == flce.FLCE_ERR_UNSUPPORTED
+
+
 def test_chunked_params_layout_and_validation(lib):
     # 4 x int64, 4 x int32
     assert ctypes.sizeof(flce.flce_chunked_params) == 48

@@ -341,7 +341,7 @@ def _sampled_check(flce, wl: si.Workload, n_rows=512, n_vocab=512, run=None):
         rows[:4] = ign[:4]
         rows = np.unique(rows)
     valid_t = inp["targets"][inp["targets"] != si.IGNORE_INDEX]
-    vids = np.unique(np.concatenate([rng.choice(c.v, n_vocab // 2, replace=False),
+    vids = np.unique(np.concatenate([rng.choice(c.v, min(n_vocab // 2, c.v), replace=False),
                                      rng.choice(valid_t, n_vocab // 2)]))
     gh_s = t2np(gh[torch.from_numpy(rows).cuda()])
     gw_s = t2np(gw[torch.from_numpy(vids).cuda()])
@@ -384,6 +384,18 @@ RAGGED_MID = si.Workload("bf16_n6000_h1600_v50257_ragged", 6000, 1600, 50257, "b
 @pytest.mark.slow
 def test_ragged_mid_size_sampled(flce_lib):
     _sampled_check(flce_lib, RAGGED_MID)
+
+
+# The largest hidden the boundary accepts: N*H*2 bytes = 2^31 - 64 KiB (every
+# 32-bit byte range the kernels form, and the 2 GiB transposed copy of hidden,
+# at their limit); a small vocabulary keeps the oracle's full pass to seconds.
+MAX_ROWS = si.Workload("bf16_n262136_h4096_v64_max_rows", 262136, 4096, 64, "bf16", 0.05, 0.1,
+                       logit_scale=0.5, softcap=30.0, ignore_frac=0.05, reduction="sum", seed=9)
+
+
+@pytest.mark.slow
+def test_max_rows_sampled(flce_lib):
+    _sampled_check(flce_lib, MAX_ROWS)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
