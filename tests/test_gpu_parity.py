@@ -76,6 +76,11 @@ SMALL_CASES = [
          weight_std=0.1),
     Case("ragged_f16_none_gwf32", 333, 136, 777, "f16", None, 1.0, None, 0.0, 0.05, "none", "f32",
          weight_std=0.1),
+    # logits in the hundreds without a cap: every exponential is taken relative
+    # to the running maximum (p is nearly one-hot, LSE ~ the row maximum)
+    Case("huge_logits_no_cap", 300, 64, 1000, "bf16", 0.1, 200.0, None, 0.0, 0.05, "sum", weight_std=0.1),
+    Case("huge_logits_no_cap_f16_zloss", 300, 64, 1000, "f16", 0.1, 200.0, None, 1e-4, 0.05, "mean",
+         weight_std=0.1),
     # H = 8: one K stage, all but its first 16 (bf16) or 32 (fp32) bytes per row
     # past the end of the rows
     Case("hidden_8_bf16", 600, 8, 3000, "bf16", 0.1, 1.0, None, 0.0, 0.05, "sum", weight_std=0.3),
